@@ -1,0 +1,152 @@
+/*
+ * flp.h -- C ABI of the fused linear selected-token log-probability library
+ * for AMD MI355X (gfx950).
+ *
+ * For token rows i = 0..N-1, vocabulary columns v = 0..V-1:
+ *
+ *   z_iv   = (hidden_i . W_v + b_v) / T_i            scaled logits (never stored)
+ *   lse_i  = log sum_v exp(z_iv)
+ *   logp_i = z_i[t_i] - lse_i     if 0 <= t_i < V, else exactly 0
+ *
+ * The operation is the one of the "Fused Linear LogP" docs page (section
+ * "Reference Semantics": linear layer, log_softmax, gather at the target;
+ * section "Tensor Contract": shapes, dtypes, float32 output
+ * z[target] - logsumexp(z)).  The optional per-row temperature and the
+ * fail-closed gates follow the "Feat/nemotron h lm head logprob cuda" page
+ * (PR #555, summary bullets); the temperature divides the biased logits.
+ * Out-of-range targets give logp = 0 and zero gradient (PR #234 inline
+ * review; PR #547 page, section "What", indexed semantics).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers on the current HIP device,
+ *     row-major and densely packed, owned by the caller.  The library
+ *     allocates nothing and keeps no state besides a once-initialised
+ *     per-device property cache; the calls are re-entrant.
+ *   - Work is enqueued on `stream` (a hipStream_t, or NULL for the default
+ *     stream) and the call returns at once.  Outputs are valid once the
+ *     stream has synchronised; device faults surface there.
+ *   - Inputs are read-only.  Outputs are overwritten, never accumulated.
+ *     No output may overlap any input or another output (checked from the
+ *     address ranges; FLP_INVALID_ARGUMENT otherwise).
+ *   - Every argument is validated before anything is enqueued.  On any
+ *     non-OK status nothing has been enqueued and no output was touched.
+ *     There is no fallback path: an unsupported case is an error.
+ *   - N = 0 returns FLP_OK and enqueues nothing.
+ *   - Results are deterministic and batch-invariant: logp, lse and each row
+ *     of d_hidden are bitwise the same whatever the other rows are, whatever
+ *     N is and wherever the row sits; d_weight and d_bias are bitwise the
+ *     same from run to run and for any backward workspace size.
+ */
+#ifndef FLP_H_
+#define FLP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum flp_status {
+  FLP_OK = 0,
+  FLP_INVALID_ARGUMENT = 1,      /* null required pointer, N < 0, V < 1, D < 1, overlap */
+  FLP_UNSUPPORTED_DTYPE = 2,     /* a dtype outside the lists below */
+  FLP_UNSUPPORTED_SHAPE = 3,     /* D % 32 != 0, or a size beyond the 64-bit index range */
+  FLP_MISALIGNED = 4,            /* hidden/weight/workspace not 16-byte aligned, others not
+                                    aligned to their element size */
+  FLP_WORKSPACE_TOO_SMALL = 5,   /* workspace_bytes below the *_workspace_bytes minimum */
+  FLP_UNSUPPORTED_DEVICE = 6,    /* current device is not gfx950 */
+  FLP_HIP_ERROR = 7              /* a HIP runtime call or kernel launch failed */
+} flp_status;
+
+typedef enum flp_dtype {
+  FLP_BF16 = 0,   /* bfloat16, 2 bytes */
+  FLP_F32 = 1,    /* IEEE binary32 */
+  FLP_I64 = 2,    /* int64 target ids */
+  FLP_I32 = 3     /* int32 target ids */
+} flp_dtype;
+
+/*
+ * Forward workspace in bytes for (N, D, V): per-row, per-vocabulary-tile
+ * partial (max, sum-of-exp) pairs and the target logits.  16-byte aligned.
+ */
+size_t flp_forward_workspace_bytes(int64_t N, int64_t D, int64_t V);
+
+/*
+ * Forward: out_logp[i] and (optionally) out_lse[i] for every row.
+ *
+ *   x_dtype      FLP_BF16 or FLP_F32: element type of hidden and weight.
+ *   hidden       [N, D] x_dtype, 16-byte aligned.
+ *   weight       [V, D] x_dtype, 16-byte aligned.
+ *   bias         [V] float32, or NULL for no bias.
+ *   targets      [N] ids of t_dtype (FLP_I64 or FLP_I32); any value is legal,
+ *                an id outside [0, V) marks the row as ignored (logp = 0).
+ *   temperature  [N] float32 (> 0, finite; not checked), or NULL for T = 1.
+ *   out_logp     [N] float32.
+ *   out_lse      [N] float32 log-sum-exp of the scaled logits, or NULL
+ *                (rollout).  logp is bitwise the same either way.
+ *   workspace    >= flp_forward_workspace_bytes(N, D, V) bytes, 16-byte
+ *                aligned; scratch, contents undefined after the call.
+ *   stream       hipStream_t to enqueue on.
+ *
+ * Requirements: D % 32 == 0, V >= 1, N >= 0.
+ */
+flp_status flp_forward(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
+                       const void* hidden, const void* weight, const float* bias,
+                       const void* targets, flp_dtype t_dtype,
+                       const float* temperature,
+                       float* out_logp, float* out_lse,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward workspace in bytes.  chunk_rows = 0 asks for the minimum (row
+ * chunks of 256); a positive chunk_rows asks for the size that lets the
+ * backward process that many rows per chunk (rounded up to a multiple of
+ * 256, capped at N rounded up).  Any workspace at least the minimum is
+ * accepted; a larger one gives larger chunks and the same bits.
+ */
+size_t flp_backward_workspace_bytes(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
+                                    flp_dtype dw_dtype, int64_t chunk_rows);
+
+/*
+ * Backward of L = sum_i grad_out[i] * logp[i]:
+ *
+ *   dz_iv     = G_i (onehot(t_i)_v - exp(z_iv - lse_i)) / T_i,
+ *               G_i = grad_out[i] if 0 <= t_i < V else 0
+ *   d_hidden  = dz W          [N, D] in x_dtype (RNE from fp32 accumulation)
+ *   d_weight  = dz^T hidden   [V, D] in dw_dtype (fp32 accumulation over the
+ *                              tokens in ascending order, one final rounding)
+ *   d_bias    = sum_i dz_i    [V] float32
+ *
+ * (PR #234, "Implementation details": grad_out * (one_hot - softmax) from the
+ * saved statistics; PR #555 summary: chunked deterministic backward whose
+ * chunking is bit-neutral.)
+ *
+ *   grad_out     [N] float32.
+ *   lse          [N] float32 as written by flp_forward for the same inputs.
+ *   hidden, weight, bias, targets, t_dtype, temperature: as in flp_forward.
+ *   d_hidden     [N, D] x_dtype, or NULL to skip.
+ *   d_weight     [V, D] dw_dtype (x_dtype or FLP_F32), or NULL to skip.
+ *   d_bias       [V] float32, or NULL to skip (allowed with bias == NULL).
+ *   workspace    >= flp_backward_workspace_bytes(N, D, V, x_dtype, dw_dtype, 0).
+ */
+flp_status flp_backward(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
+                        const float* grad_out, const float* lse,
+                        const void* hidden, const void* weight, const float* bias,
+                        const void* targets, flp_dtype t_dtype,
+                        const float* temperature,
+                        void* d_hidden, void* d_weight, flp_dtype dw_dtype,
+                        float* d_bias,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* flp_status_string(flp_status status);
+
+/* Build provenance: library version, target, kernel ids and tile shapes. */
+const char* flp_build_info(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLP_H_ */

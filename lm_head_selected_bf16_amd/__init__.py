@@ -1,0 +1,23 @@
+"""Fused linear selected-token log-probability for AMD MI355X (gfx950).
+
+    logp = log_softmax((hidden @ W^T + b) / T)[target]     (0 for out-of-range targets)
+
+and its backward to hidden, W and b, computed by hand-written HIP kernels in
+libflp.so behind the C ABI of include/flp.h.  This package holds the build
+script, the ctypes binding (same names as the C ABI) and a thin PyTorch
+wrapper with autograd.
+"""
+from ._abi import (FLP_BF16, FLP_F32, FLP_I32, FLP_I64, FLP_OK, FlpError,  # noqa: F401
+                   flp_backward, flp_backward_workspace_bytes, flp_build_info, flp_forward,
+                   flp_forward_workspace_bytes, flp_status_string, load)
+from .torch_ops import (LinearLogp, backward, backward_workspace_bytes,  # noqa: F401
+                        default_backward_workspace_bytes, forward, linear_logp,
+                        linear_logp_with_lse)
+
+__all__ = [
+    "FLP_BF16", "FLP_F32", "FLP_I32", "FLP_I64", "FLP_OK", "FlpError",
+    "flp_forward", "flp_backward", "flp_forward_workspace_bytes", "flp_backward_workspace_bytes",
+    "flp_status_string", "flp_build_info", "load",
+    "LinearLogp", "forward", "backward", "backward_workspace_bytes",
+    "default_backward_workspace_bytes", "linear_logp", "linear_logp_with_lse",
+]

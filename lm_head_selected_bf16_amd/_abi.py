@@ -1,0 +1,110 @@
+"""ctypes binding of libflp.so: the C ABI of include/flp.h, name for name.
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+kernels behind these calls; there is no other implementation to fall back on.
+If the library is missing, loading fails with an error that says how to build it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflp.so")
+
+# flp_dtype
+FLP_BF16, FLP_F32, FLP_I64, FLP_I32 = 0, 1, 2, 3
+# flp_status
+STATUS_NAMES = {
+    0: "FLP_OK",
+    1: "FLP_INVALID_ARGUMENT",
+    2: "FLP_UNSUPPORTED_DTYPE",
+    3: "FLP_UNSUPPORTED_SHAPE",
+    4: "FLP_MISALIGNED",
+    5: "FLP_WORKSPACE_TOO_SMALL",
+    6: "FLP_UNSUPPORTED_DEVICE",
+    7: "FLP_HIP_ERROR",
+}
+FLP_OK = 0
+
+# Every symbol include/flp.h declares, with (restype, argtypes).
+_i64, _sz, _vp, _fp, _int = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int
+SIGNATURES = {
+    "flp_forward_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+    "flp_forward": (_int, [_i64, _i64, _i64, _int, _vp, _vp, _fp, _vp, _int, _fp, _fp, _fp, _vp,
+                           _sz, _vp]),
+    "flp_backward_workspace_bytes": (_sz, [_i64, _i64, _i64, _int, _int, _i64]),
+    "flp_backward": (_int, [_i64, _i64, _i64, _int, _fp, _fp, _vp, _vp, _fp, _vp, _int, _fp, _vp,
+                            _vp, _int, _fp, _vp, _sz, _vp]),
+    "flp_status_string": (ctypes.c_char_p, [_int]),
+    "flp_build_info": (ctypes.c_char_p, []),
+}
+
+_lock = threading.Lock()
+_lib = None
+
+
+class FlpError(RuntimeError):
+    """A non-OK status returned by the library."""
+
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {status_string(status)}")
+
+
+def load() -> ctypes.CDLL:
+    """Load libflp.so from the package directory (raises if it was not built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise ImportError(
+                    f"{LIB_PATH} is missing: build it with `python -m lm_head_selected_bf16_amd.build` "
+                    "(hipcc, gfx950).  There is no other implementation of this operator.")
+            lib = ctypes.CDLL(LIB_PATH)
+            for name, (res, args) in SIGNATURES.items():
+                fn = getattr(lib, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    try:
+        return load().flp_status_string(int(status)).decode()
+    except ImportError:
+        return STATUS_NAMES.get(int(status), f"status {status}")
+
+
+def flp_forward_workspace_bytes(N: int, D: int, V: int) -> int:
+    return int(load().flp_forward_workspace_bytes(N, D, V))
+
+
+def flp_backward_workspace_bytes(N: int, D: int, V: int, x_dtype: int, dw_dtype: int,
+                                 chunk_rows: int = 0) -> int:
+    return int(load().flp_backward_workspace_bytes(N, D, V, x_dtype, dw_dtype, chunk_rows))
+
+
+def flp_forward(N, D, V, x_dtype, hidden, weight, bias, targets, t_dtype, temperature,
+                out_logp, out_lse, workspace, workspace_bytes, stream) -> int:
+    """Raw call: every pointer argument is an int address (0 for NULL)."""
+    return int(load().flp_forward(N, D, V, x_dtype, hidden, weight, bias, targets, t_dtype,
+                                  temperature, out_logp, out_lse, workspace, workspace_bytes, stream))
+
+
+def flp_backward(N, D, V, x_dtype, grad_out, lse, hidden, weight, bias, targets, t_dtype,
+                 temperature, d_hidden, d_weight, dw_dtype, d_bias, workspace, workspace_bytes,
+                 stream) -> int:
+    """Raw call: every pointer argument is an int address (0 for NULL)."""
+    return int(load().flp_backward(N, D, V, x_dtype, grad_out, lse, hidden, weight, bias, targets,
+                                   t_dtype, temperature, d_hidden, d_weight, dw_dtype, d_bias,
+                                   workspace, workspace_bytes, stream))
+
+
+def flp_status_string(status: int) -> str:
+    return load().flp_status_string(int(status)).decode()
+
+
+def flp_build_info() -> str:
+    return load().flp_build_info().decode()

@@ -1,0 +1,217 @@
+// C ABI entry points (include/flp.h): validate synchronously, then enqueue the
+// kernels on the caller's stream.  Fail closed: no fallback path exists.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "flp_launch.h"
+
+namespace {
+
+using namespace flp;
+
+// Per-device cache of "is gfx950": 0 = unknown, 1 = yes, 2 = no.
+std::atomic<int> g_arch[64];
+
+flp_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FLP_UNSUPPORTED_DEVICE;
+  if (dev < 64) {
+    const int c = g_arch[dev].load(std::memory_order_relaxed);
+    if (c == 1) return FLP_OK;
+    if (c == 2) return FLP_UNSUPPORTED_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FLP_HIP_ERROR;
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 64) g_arch[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? FLP_OK : FLP_UNSUPPORTED_DEVICE;
+}
+
+inline char* at(void* base, size_t off) { return static_cast<char*>(base) + off; }
+
+}  // namespace
+
+extern "C" {
+
+size_t flp_forward_workspace_bytes(int64_t N, int64_t D, int64_t V) {
+  if (N < 0 || D < 1 || V < 1) return 0;
+  return fwd_layout(N, D, V).total;
+}
+
+flp_status flp_forward(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype, const void* hidden,
+                       const void* weight, const float* bias, const void* targets,
+                       flp_dtype t_dtype, const float* temperature, float* out_logp,
+                       float* out_lse, void* workspace, size_t workspace_bytes, void* stream) {
+  flp_status st = validate_forward(N, D, V, x_dtype, hidden, weight, bias, targets, t_dtype,
+                                   temperature, out_logp, out_lse, workspace, workspace_bytes);
+  if (st != FLP_OK || N == 0) return st;
+  if ((st = check_device()) != FLP_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const FwdLayout L = fwd_layout(N, D, V);
+  FwdArgs f;
+  f.hidden = hidden;
+  f.weight = weight;
+  f.bias = bias;
+  f.targets = targets;
+  f.t64 = t_dtype == FLP_I64;
+  f.temperature = temperature;
+  f.N = N;
+  f.D = D;
+  f.V = V;
+  f.part = reinterpret_cast<float2*>(at(workspace, L.part_off));
+  f.zt = reinterpret_cast<float*>(at(workspace, L.zt_off));
+  if (launch_forward(x_dtype, f, s) != hipSuccess) return FLP_HIP_ERROR;
+  MergeArgs m;
+  m.part = f.part;
+  m.zt = f.zt;
+  m.targets = targets;
+  m.t64 = f.t64;
+  m.N = N;
+  m.V = V;
+  m.n_vt = L.n_vt;
+  m.logp = out_logp;
+  m.lse = out_lse;
+  if (launch_merge(m, s) != hipSuccess) return FLP_HIP_ERROR;
+  return FLP_OK;
+}
+
+size_t flp_backward_workspace_bytes(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
+                                    flp_dtype dw_dtype, int64_t chunk_rows) {
+  if (N < 0 || D < 1 || V < 1 || chunk_rows < 0) return 0;
+  if (x_dtype != FLP_BF16 && x_dtype != FLP_F32) return 0;
+  if (N == 0) return 0;
+  const int64_t chunk = chunk_rows == 0 ? kRowQuantum : chunk_rows;
+  return bwd_layout_for_chunk(N, D, V, x_dtype, dw_dtype, chunk, true, true, true).total;
+}
+
+flp_status flp_backward(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
+                        const float* grad_out, const float* lse, const void* hidden,
+                        const void* weight, const float* bias, const void* targets,
+                        flp_dtype t_dtype, const float* temperature, void* d_hidden,
+                        void* d_weight, flp_dtype dw_dtype, float* d_bias, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  flp_status st = validate_backward(N, D, V, x_dtype, grad_out, lse, hidden, weight, bias, targets,
+                                    t_dtype, temperature, d_hidden, d_weight, dw_dtype, d_bias,
+                                    workspace, workspace_bytes);
+  if (st != FLP_OK || N == 0) return st;
+  if (!d_hidden && !d_weight && !d_bias) return FLP_OK;
+  if ((st = check_device()) != FLP_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const BwdLayout L = bwd_layout_for_bytes(N, D, V, x_dtype, dw_dtype, workspace_bytes,
+                                           d_hidden != nullptr, d_weight != nullptr,
+                                           d_bias != nullptr);
+  const size_t xs = dtype_size(x_dtype);
+  const size_t ts = dtype_size(t_dtype);
+  void* dz = d_hidden ? at(workspace, L.dz_off) : nullptr;
+  void* dzT = d_weight ? at(workspace, L.dzt_off) : nullptr;
+  void* hT = d_weight ? at(workspace, L.ht_off) : nullptr;
+  float* dbp = d_bias ? reinterpret_cast<float*>(at(workspace, L.dbp_off)) : nullptr;
+  float* acc = nullptr;
+  if (d_weight) {
+    if (dw_dtype == FLP_F32)
+      acc = static_cast<float*>(d_weight);
+    else if (L.use_acc)
+      acc = reinterpret_cast<float*>(at(workspace, L.acc_off));
+  }
+  for (int64_t c = 0; c < L.n_chunks; ++c) {
+    const int64_t r0 = c * L.chunk;
+    const int64_t rows = (N - r0 < L.chunk) ? N - r0 : L.chunk;
+    const bool last = c + 1 == L.n_chunks;
+    const void* h_chunk = static_cast<const char*>(hidden) + size_t(r0) * D * xs;
+    DzArgs z;
+    z.hidden = h_chunk;
+    z.weight = weight;
+    z.bias = bias;
+    z.targets = static_cast<const char*>(targets) + size_t(r0) * ts;
+    z.t64 = t_dtype == FLP_I64;
+    z.temperature = temperature ? temperature + r0 : nullptr;
+    z.grad_out = grad_out + r0;
+    z.lse = lse + r0;
+    z.rows = rows;
+    z.D = D;
+    z.V = V;
+    z.ldz = L.ldz;
+    z.ldt = L.ldt;
+    z.dz = dz;
+    z.dzT = dzT;
+    z.dbias_part = dbp;
+    if (launch_dz(x_dtype, z, s) != hipSuccess) return FLP_HIP_ERROR;
+    if (d_hidden) {
+      GemmArgs g;
+      g.a = dz;
+      g.b = weight;
+      g.lda_b = L.ldz * int64_t(xs);
+      g.ldb_b = D * int64_t(xs);
+      g.M = rows;
+      g.N = D;
+      g.K = V;
+      g.out = static_cast<char*>(d_hidden) + size_t(r0) * D * xs;
+      g.ldo = D;
+      g.acc = nullptr;
+      g.load_acc = 0;
+      g.store_acc = 0;
+      if (launch_dx(x_dtype, g, s) != hipSuccess) return FLP_HIP_ERROR;
+    }
+    if (d_weight) {
+      if (launch_transpose(x_dtype, h_chunk, rows, round_up(rows, 64), D, D, hT, L.ldt, s) !=
+          hipSuccess)
+        return FLP_HIP_ERROR;
+      GemmArgs g;
+      g.a = dzT;
+      g.b = hT;
+      g.lda_b = L.ldt * int64_t(xs);
+      g.ldb_b = L.ldt * int64_t(xs);
+      g.M = V;
+      g.N = D;
+      g.K = rows;
+      g.out = d_weight;
+      g.ldo = D;
+      g.acc = acc;
+      g.load_acc = (acc != nullptr && c > 0) ? 1 : 0;
+      g.store_acc = (acc != nullptr && (dw_dtype == FLP_F32 || !last)) ? 1 : 0;
+      if (launch_dw(x_dtype, g, s) != hipSuccess) return FLP_HIP_ERROR;
+    }
+    if (d_bias) {
+      if (launch_dbias_fold(dbp, (rows + kDzRowTile - 1) / kDzRowTile, L.ldz, V, d_bias, c == 0,
+                            s) != hipSuccess)
+        return FLP_HIP_ERROR;
+    }
+  }
+  return FLP_OK;
+}
+
+const char* flp_status_string(flp_status status) {
+  switch (status) {
+    case FLP_OK: return "FLP_OK";
+    case FLP_INVALID_ARGUMENT: return "FLP_INVALID_ARGUMENT: null pointer, negative size or overlapping buffers";
+    case FLP_UNSUPPORTED_DTYPE: return "FLP_UNSUPPORTED_DTYPE";
+    case FLP_UNSUPPORTED_SHAPE: return "FLP_UNSUPPORTED_SHAPE: D must be a multiple of 32";
+    case FLP_MISALIGNED: return "FLP_MISALIGNED";
+    case FLP_WORKSPACE_TOO_SMALL: return "FLP_WORKSPACE_TOO_SMALL";
+    case FLP_UNSUPPORTED_DEVICE: return "FLP_UNSUPPORTED_DEVICE: needs gfx950 (MI355X)";
+    case FLP_HIP_ERROR: return "FLP_HIP_ERROR";
+  }
+  return "FLP_UNKNOWN_STATUS";
+}
+
+const char* flp_build_info(void) {
+  static const std::string info = [] {
+    char buf[1024];
+    std::snprintf(buf, sizeof(buf), "flp 0.1 gfx950 vocab_tile=%lld row_quantum=%lld git=%s | %s",
+                  (long long)kVocabTile, (long long)kRowQuantum,
+#ifdef FLP_GIT_HASH
+                  FLP_GIT_HASH,
+#else
+                  "unknown",
+#endif
+                  kernel_ids());
+    return std::string(buf);
+  }();
+  return info.c_str();
+}
+
+}  // extern "C"

@@ -1,0 +1,69 @@
+// Kernel argument blocks and launchers (implemented in flp_kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "flp_plan.h"
+
+namespace flp {
+
+struct FwdArgs {
+  const void* hidden;
+  const void* weight;
+  const float* bias;
+  const void* targets;
+  int t64;
+  const float* temperature;
+  int64_t N, D, V;
+  float2* part;     // [n_vt][N]
+  float* zt;        // [N]
+};
+struct MergeArgs {
+  const float2* part;
+  const float* zt;
+  const void* targets;
+  int t64;
+  int64_t N, V, n_vt;
+  float* logp;
+  float* lse;       // may be null
+};
+struct DzArgs {
+  const void* hidden;   // chunk start
+  const void* weight;
+  const float* bias;
+  const void* targets;  // chunk start
+  int t64;
+  const float* temperature;  // chunk start or null
+  const float* grad_out;     // chunk start
+  const float* lse;          // chunk start
+  int64_t rows, D, V, ldz, ldt;
+  void* dz;                  // [rows_alloc][ldz], or null when d_hidden is not needed
+  void* dzT;                 // [ldz][ldt] (tokens contiguous), or null when d_weight is not needed
+  float* dbias_part;         // [rows_alloc / kDzRowTile][ldz] or null
+};
+struct GemmArgs {
+  const void* a;   // M-side operand
+  const void* b;   // N-side operand
+  int64_t lda_b, ldb_b;  // row strides in bytes
+  int64_t M, N, K;
+  void* out;             // output (x dtype or fp32)
+  int64_t ldo;           // elements
+  float* acc;            // fp32 accumulator [M][N] (dW) or null
+  int load_acc;          // continue from acc
+  int store_acc;         // store fp32 to acc (else store to out in x dtype)
+};
+
+hipError_t launch_forward(flp_dtype x, const FwdArgs& a, hipStream_t s);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+hipError_t launch_dz(flp_dtype x, const DzArgs& a, hipStream_t s);
+hipError_t launch_dx(flp_dtype x, const GemmArgs& a, hipStream_t s);
+hipError_t launch_dw(flp_dtype x, const GemmArgs& a, hipStream_t s);
+// dst[c][r] = src[r][c] for r < rows, c < cols (row strides in elements); rows
+// [rows, rows_pad) of dst's columns are zero-filled.
+hipError_t launch_transpose(flp_dtype x, const void* src, int64_t rows, int64_t rows_pad, int64_t cols,
+                            int64_t ld_src, void* dst, int64_t ld_dst, hipStream_t s);
+hipError_t launch_dbias_fold(const float* part, int64_t n_parts, int64_t ldz, int64_t V,
+                             float* d_bias, int init, hipStream_t s);
+const char* kernel_ids();
+
+}  // namespace flp

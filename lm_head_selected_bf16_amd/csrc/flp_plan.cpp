@@ -1,0 +1,181 @@
+// Workspace layouts and fail-closed argument validation for the C ABI.
+// Pure host arithmetic: no HIP call, no pointer is ever dereferenced, so every
+// gate can be exercised on a machine without a GPU.
+#include "flp_plan.h"
+
+#include <algorithm>
+#include <limits>
+
+namespace flp {
+
+namespace {
+
+constexpr int64_t kMaxIndex = std::numeric_limits<int64_t>::max() / 16;
+
+bool mul_ok(int64_t a, int64_t b) { return a == 0 || b <= kMaxIndex / a; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Span {
+  uintptr_t lo = 0, hi = 0;
+  bool live() const { return hi > lo; }
+};
+
+Span span(const void* p, size_t bytes) {
+  Span s;
+  if (p != nullptr && bytes > 0) {
+    s.lo = reinterpret_cast<uintptr_t>(p);
+    s.hi = s.lo + bytes;
+  }
+  return s;
+}
+
+bool overlap(const Span& a, const Span& b) {
+  return a.live() && b.live() && a.lo < b.hi && b.lo < a.hi;
+}
+
+// Every output span must be disjoint from every input span and from every other
+// output span.
+bool any_alias(const Span* outs, int n_out, const Span* ins, int n_in) {
+  for (int i = 0; i < n_out; ++i) {
+    for (int j = 0; j < n_in; ++j)
+      if (overlap(outs[i], ins[j])) return true;
+    for (int j = i + 1; j < n_out; ++j)
+      if (overlap(outs[i], outs[j])) return true;
+  }
+  return false;
+}
+
+flp_status check_dims(int64_t N, int64_t D, int64_t V, flp_dtype x, flp_dtype t) {
+  if (N < 0 || D < 1 || V < 1) return FLP_INVALID_ARGUMENT;
+  if (x != FLP_BF16 && x != FLP_F32) return FLP_UNSUPPORTED_DTYPE;
+  if (t != FLP_I64 && t != FLP_I32) return FLP_UNSUPPORTED_DTYPE;
+  if (D % 32 != 0) return FLP_UNSUPPORTED_SHAPE;
+  const int64_t rows = std::max<int64_t>(round_up(std::max<int64_t>(N, 1), kRowQuantum), 1);
+  const int64_t ldz = round_up(V, kVocabTile);
+  if (!mul_ok(rows, D) || !mul_ok(ldz, D) || !mul_ok(rows, ldz) ||
+      !mul_ok(ceil_div(V, kVocabTile), rows))
+    return FLP_UNSUPPORTED_SHAPE;
+  // Grid limits: row tiles x vocab tiles and the output tiles of the GEMMs.
+  if (ceil_div(rows, 16) * ceil_div(V, kVocabTile) > (int64_t(1) << 31) - 1) return FLP_UNSUPPORTED_SHAPE;
+  return FLP_OK;
+}
+
+}  // namespace
+
+FwdLayout fwd_layout(int64_t N, int64_t /*D*/, int64_t V) {
+  FwdLayout L;
+  L.n_vt = ceil_div(V, kVocabTile);
+  L.part_off = 0;
+  L.zt_off = align_up(size_t(L.n_vt) * size_t(N) * 8);
+  L.total = L.zt_off + align_up(size_t(N) * 4);
+  return L;
+}
+
+BwdLayout bwd_layout_for_chunk(int64_t N, int64_t D, int64_t V, flp_dtype x, flp_dtype dw,
+                               int64_t chunk, bool need_dh, bool need_dw, bool need_db) {
+  BwdLayout L;
+  const int64_t full = round_up(std::max<int64_t>(N, 1), kRowQuantum);
+  chunk = std::min(round_up(std::max<int64_t>(chunk, 1), kRowQuantum), full);
+  const size_t xs = dtype_size(x);
+  L.chunk = chunk;
+  L.n_chunks = ceil_div(std::max<int64_t>(N, 1), chunk);
+  L.ldz = round_up(V, kVocabTile);
+  L.ldt = chunk;
+  size_t off = 0;
+  L.dz_off = off;
+  if (need_dh) off += align_up(size_t(chunk) * size_t(L.ldz) * xs);
+  L.dzt_off = off;
+  if (need_dw) off += align_up(size_t(L.ldz) * size_t(chunk) * xs);
+  L.ht_off = off;
+  if (need_dw) off += align_up(size_t(D) * size_t(chunk) * xs);
+  L.dbp_off = off;
+  if (need_db) off += align_up(size_t(chunk / kDzRowTile) * size_t(L.ldz) * 4);
+  L.acc_off = off;
+  L.use_acc = need_dw && dw != FLP_F32 && L.n_chunks > 1;
+  if (L.use_acc) off += align_up(size_t(V) * size_t(D) * 4);
+  L.total = std::max<size_t>(off, kAlign);
+  return L;
+}
+
+BwdLayout bwd_layout_for_bytes(int64_t N, int64_t D, int64_t V, flp_dtype x, flp_dtype dw,
+                               size_t bytes, bool need_dh, bool need_dw, bool need_db) {
+  const int64_t full = round_up(std::max<int64_t>(N, 1), kRowQuantum);
+  BwdLayout L = bwd_layout_for_chunk(N, D, V, x, dw, full, need_dh, need_dw, need_db);
+  if (L.total <= bytes) return L;
+  // Several chunks: the fp32 accumulator (if any) plus per-chunk buffers.
+  const size_t ldz = size_t(round_up(V, kVocabTile));
+  const size_t xs = dtype_size(x);
+  const size_t q = size_t(kRowQuantum);
+  const size_t per_quantum = (need_dh ? q * ldz * xs : 0) + (need_dw ? q * (ldz + size_t(D)) * xs : 0) +
+                             (need_db ? (q / size_t(kDzRowTile)) * ldz * 4 : 0);
+  const size_t fixed = (need_dw && dw != FLP_F32) ? align_up(size_t(V) * size_t(D) * 4) : 0;
+  int64_t nq = 0;
+  if (per_quantum > 0 && bytes > fixed + 5 * kAlign) nq = int64_t((bytes - fixed - 5 * kAlign) / per_quantum);
+  nq = std::min<int64_t>(nq, full / kRowQuantum);
+  for (; nq >= 1; --nq) {
+    L = bwd_layout_for_chunk(N, D, V, x, dw, nq * kRowQuantum, need_dh, need_dw, need_db);
+    if (L.total <= bytes) return L;
+  }
+  L = BwdLayout();
+  return L;
+}
+
+flp_status validate_forward(int64_t N, int64_t D, int64_t V, flp_dtype x, const void* hidden,
+                            const void* weight, const float* bias, const void* targets,
+                            flp_dtype t, const float* temperature, const float* out_logp,
+                            const float* out_lse, const void* workspace,
+                            size_t workspace_bytes) {
+  flp_status st = check_dims(N, D, V, x, t);
+  if (st != FLP_OK) return st;
+  if (N == 0) return FLP_OK;
+  if (!hidden || !weight || !targets || !out_logp || !workspace) return FLP_INVALID_ARGUMENT;
+  if (!aligned(hidden, 16) || !aligned(weight, 16) || !aligned(workspace, 16) ||
+      !aligned(bias, 4) || !aligned(temperature, 4) || !aligned(out_logp, 4) ||
+      !aligned(out_lse, 4) || !aligned(targets, dtype_size(t)))
+    return FLP_MISALIGNED;
+  const size_t xs = dtype_size(x);
+  const Span ins[] = {span(hidden, size_t(N) * D * xs), span(weight, size_t(V) * D * xs),
+                      span(bias, size_t(V) * 4), span(targets, size_t(N) * dtype_size(t)),
+                      span(temperature, size_t(N) * 4)};
+  const Span outs[] = {span(out_logp, size_t(N) * 4), span(out_lse, size_t(N) * 4),
+                       span(workspace, workspace_bytes)};
+  if (any_alias(outs, 3, ins, 5)) return FLP_INVALID_ARGUMENT;
+  if (workspace_bytes < fwd_layout(N, D, V).total) return FLP_WORKSPACE_TOO_SMALL;
+  return FLP_OK;
+}
+
+flp_status validate_backward(int64_t N, int64_t D, int64_t V, flp_dtype x, const float* grad_out,
+                             const float* lse, const void* hidden, const void* weight,
+                             const float* bias, const void* targets, flp_dtype t,
+                             const float* temperature, const void* d_hidden,
+                             const void* d_weight, flp_dtype dw, const float* d_bias,
+                             const void* workspace, size_t workspace_bytes) {
+  flp_status st = check_dims(N, D, V, x, t);
+  if (st != FLP_OK) return st;
+  if (dw != x && dw != FLP_F32) return FLP_UNSUPPORTED_DTYPE;
+  if (N == 0) return FLP_OK;
+  if (!grad_out || !lse || !hidden || !weight || !targets) return FLP_INVALID_ARGUMENT;
+  if (!d_hidden && !d_weight && !d_bias) return FLP_OK;
+  if (!workspace) return FLP_INVALID_ARGUMENT;
+  const size_t xs = dtype_size(x);
+  if (!aligned(hidden, 16) || !aligned(weight, 16) || !aligned(workspace, 16) ||
+      !aligned(grad_out, 4) || !aligned(lse, 4) || !aligned(bias, 4) ||
+      !aligned(temperature, 4) || !aligned(targets, dtype_size(t)) ||
+      !aligned(d_hidden, 16) || !aligned(d_weight, 16) || !aligned(d_bias, 4))
+    return FLP_MISALIGNED;
+  const Span ins[] = {span(grad_out, size_t(N) * 4), span(lse, size_t(N) * 4),
+                      span(hidden, size_t(N) * D * xs), span(weight, size_t(V) * D * xs),
+                      span(bias, size_t(V) * 4), span(targets, size_t(N) * dtype_size(t)),
+                      span(temperature, size_t(N) * 4)};
+  const Span outs[] = {span(d_hidden, size_t(N) * D * xs),
+                       span(d_weight, size_t(V) * D * dtype_size(dw)),
+                       span(d_bias, size_t(V) * 4), span(workspace, workspace_bytes)};
+  if (any_alias(outs, 4, ins, 7)) return FLP_INVALID_ARGUMENT;
+  const BwdLayout L = bwd_layout_for_bytes(N, D, V, x, dw, workspace_bytes, d_hidden != nullptr,
+                                           d_weight != nullptr, d_bias != nullptr);
+  if (L.chunk == 0) return FLP_WORKSPACE_TOO_SMALL;
+  return FLP_OK;
+}
+
+}  // namespace flp

@@ -1,0 +1,74 @@
+// Host-side planning shared by the C-ABI layer and the kernels: the numeric
+// constants of the reduction topology, workspace layouts and argument
+// validation.  Plain C++, no HIP dependency, never dereferences a pointer.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/flp.h"
+
+namespace flp {
+
+// Vocabulary tile width of the forward and dlogits kernels.  It fixes the
+// reduction topology of every row (online max / sum-of-exp per 256-column
+// tile, then an ascending fold over tiles), so it is a constant of the
+// numerics, not a tuning knob.
+constexpr int64_t kVocabTile = 256;
+// Row granularity of backward chunks (multiple of every row tile and K step).
+constexpr int64_t kRowQuantum = 256;
+// Row tile of the dlogits kernel: one d_bias partial row per tile.
+constexpr int64_t kDzRowTile = 128;
+constexpr size_t kAlign = 256;
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+inline size_t align_up(size_t a) { return (a + kAlign - 1) / kAlign * kAlign; }
+
+inline size_t dtype_size(flp_dtype t) {
+  switch (t) {
+    case FLP_BF16: return 2;
+    case FLP_F32: return 4;
+    case FLP_I64: return 8;
+    case FLP_I32: return 4;
+  }
+  return 0;
+}
+
+// ---- forward workspace: [n_vt][N] (max, sum) pairs, then [N] target logits ----
+struct FwdLayout {
+  int64_t n_vt = 0;
+  size_t part_off = 0, zt_off = 0, total = 0;
+};
+FwdLayout fwd_layout(int64_t N, int64_t D, int64_t V);
+
+// ---- backward workspace: dz chunk, d_bias partials, fp32 d_weight accumulator ----
+struct BwdLayout {
+  int64_t chunk = 0;      // rows per chunk (multiple of kRowQuantum)
+  int64_t n_chunks = 0;
+  int64_t ldz = 0;        // row stride of dz in elements (V rounded up to kVocabTile)
+  int64_t ldt = 0;        // row stride of dz^T and hidden^T in elements (= chunk)
+  size_t dz_off = 0, dzt_off = 0, ht_off = 0, dbp_off = 0, acc_off = 0, total = 0;
+  bool use_acc = false;   // fp32 d_weight accumulator in the workspace
+};
+// Size for a given chunk; need_* say which outputs are requested.
+BwdLayout bwd_layout_for_chunk(int64_t N, int64_t D, int64_t V, flp_dtype x, flp_dtype dw,
+                               int64_t chunk, bool need_dh, bool need_dw, bool need_db);
+// Largest chunk that fits `bytes` (chunk = 0 in the result when nothing fits).
+BwdLayout bwd_layout_for_bytes(int64_t N, int64_t D, int64_t V, flp_dtype x, flp_dtype dw,
+                               size_t bytes, bool need_dh, bool need_dw, bool need_db);
+
+// ---- validation (pure host logic; never dereferences a pointer) ----
+flp_status validate_forward(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
+                            const void* hidden, const void* weight, const float* bias,
+                            const void* targets, flp_dtype t_dtype, const float* temperature,
+                            const float* out_logp, const float* out_lse,
+                            const void* workspace, size_t workspace_bytes);
+flp_status validate_backward(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
+                             const float* grad_out, const float* lse,
+                             const void* hidden, const void* weight, const float* bias,
+                             const void* targets, flp_dtype t_dtype, const float* temperature,
+                             const void* d_hidden, const void* d_weight, flp_dtype dw_dtype,
+                             const float* d_bias, const void* workspace, size_t workspace_bytes);
+
+}  // namespace flp

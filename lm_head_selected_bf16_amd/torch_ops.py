@@ -1,0 +1,176 @@
+"""PyTorch-facing wrapper of the C ABI: device buffers, streams and autograd.
+
+Argument marshalling only: shapes are checked and flattened, outputs and
+workspaces are allocated with torch on the inputs' device, pointers and the
+current HIP stream are passed to libflp.so.  Nothing here computes any part of
+the operator.
+
+Semantics ("Fused Linear LogP" docs page, sections "Entry Point" and "Tensor
+Contract"): hidden [B, S, D] or [N, D], weight [V, D], targets [B, S] or [N]
+(int64 or int32), optional float32 bias [V]; output float32 with the leading
+shape of targets.  The optional per-row temperature [B, S] / [N] divides the
+logits of its row (PR #555 summary).  Gradients flow to hidden, weight and bias;
+targets and temperature are not differentiable.
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from . import _abi
+from ._abi import FLP_BF16, FLP_F32, FLP_I32, FLP_I64, FLP_OK, FlpError
+
+# Default cap on the backward workspace: a larger workspace only means larger row
+# chunks (same bits); 16 GiB keeps a whole 16384-row chunk of dz and dz^T.
+DEFAULT_BWD_WORKSPACE = 16 << 30
+
+_X_DTYPES = {torch.bfloat16: FLP_BF16, torch.float32: FLP_F32}
+_T_DTYPES = {torch.int64: FLP_I64, torch.int32: FLP_I32}
+
+
+def _ptr(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+def _stream(device: torch.device) -> int:
+    return int(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(fn: str, status: int) -> None:
+    if status != FLP_OK:
+        raise FlpError(fn, status)
+
+
+def _prepare(hidden, weight, targets, bias, temperature):
+    if hidden.dtype not in _X_DTYPES or weight.dtype != hidden.dtype:
+        raise TypeError("hidden and weight must both be bfloat16 or both float32")
+    if targets.dtype not in _T_DTYPES:
+        raise TypeError("targets must be int64 or int32")
+    if not (hidden.is_cuda and weight.is_cuda and targets.is_cuda):
+        raise ValueError("hidden, weight and targets must be on the GPU")
+    for name, t in (("hidden", hidden), ("weight", weight), ("targets", targets),
+                    ("bias", bias), ("temperature", temperature)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if weight.dim() != 2 or hidden.shape[-1] != weight.shape[1]:
+        raise ValueError("weight must be [V, D] with D = hidden.shape[-1]")
+    lead = tuple(targets.shape)
+    if tuple(hidden.shape[:-1]) != lead:
+        raise ValueError("hidden leading shape must equal the targets shape")
+    D = int(hidden.shape[-1])
+    V = int(weight.shape[0])
+    h2 = hidden.reshape(-1, D)
+    t1 = targets.reshape(-1)
+    N = int(t1.shape[0])
+    if bias is not None and (bias.dtype != torch.float32 or tuple(bias.shape) != (V,)):
+        raise ValueError("bias must be float32 [V]")
+    temp1 = None
+    if temperature is not None:
+        if temperature.dtype != torch.float32 or tuple(temperature.shape) != lead:
+            raise ValueError("temperature must be float32 with the targets shape")
+        temp1 = temperature.reshape(-1)
+    return h2, t1, temp1, lead, N, D, V
+
+
+def forward(hidden: torch.Tensor, weight: torch.Tensor, targets: torch.Tensor,
+            bias: Optional[torch.Tensor] = None, temperature: Optional[torch.Tensor] = None,
+            return_lse: bool = True, workspace: Optional[torch.Tensor] = None
+            ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """logp (and lse) float32 with the targets' leading shape, through flp_forward."""
+    h2, t1, temp1, lead, N, D, V = _prepare(hidden, weight, targets, bias, temperature)
+    dev = hidden.device
+    logp = torch.empty(lead, dtype=torch.float32, device=dev)
+    lse = torch.empty(lead, dtype=torch.float32, device=dev) if return_lse else None
+    need = _abi.flp_forward_workspace_bytes(N, D, V)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    st = _abi.flp_forward(N, D, V, _X_DTYPES[hidden.dtype], _ptr(h2), _ptr(weight), _ptr(bias),
+                          _ptr(t1), _T_DTYPES[targets.dtype], _ptr(temp1), _ptr(logp), _ptr(lse),
+                          _ptr(workspace), workspace.numel() * workspace.element_size(),
+                          _stream(dev))
+    _check("flp_forward", st)
+    return logp, lse
+
+
+def backward_workspace_bytes(N: int, D: int, V: int, x_dtype: torch.dtype,
+                             dw_dtype: Optional[torch.dtype] = None, chunk_rows: int = 0) -> int:
+    dw = _X_DTYPES[x_dtype if dw_dtype is None else dw_dtype]
+    return _abi.flp_backward_workspace_bytes(N, D, V, _X_DTYPES[x_dtype], dw, chunk_rows)
+
+
+def default_backward_workspace_bytes(N: int, D: int, V: int, x_dtype: torch.dtype,
+                                     dw_dtype: Optional[torch.dtype] = None,
+                                     cap: int = DEFAULT_BWD_WORKSPACE) -> int:
+    """The whole batch as one chunk if that fits under ``cap``, else the minimum
+    plus as many 256-row quanta as fit (same bits either way)."""
+    full = backward_workspace_bytes(N, D, V, x_dtype, dw_dtype, chunk_rows=max(N, 1))
+    if full <= cap:
+        return full
+    lo = backward_workspace_bytes(N, D, V, x_dtype, dw_dtype, chunk_rows=0)
+    return max(lo, cap)
+
+
+def backward(grad_out: torch.Tensor, lse: torch.Tensor, hidden: torch.Tensor, weight: torch.Tensor,
+             targets: torch.Tensor, bias: Optional[torch.Tensor] = None,
+             temperature: Optional[torch.Tensor] = None, need_hidden: bool = True,
+             need_weight: bool = True, need_bias: Optional[bool] = None,
+             dw_dtype: Optional[torch.dtype] = None, workspace_bytes: Optional[int] = None,
+             workspace: Optional[torch.Tensor] = None):
+    """(d_hidden, d_weight, d_bias) through flp_backward; unrequested ones are None."""
+    h2, t1, temp1, lead, N, D, V = _prepare(hidden, weight, targets, bias, temperature)
+    dev = hidden.device
+    if need_bias is None:
+        need_bias = bias is not None
+    if grad_out.dtype != torch.float32 or tuple(grad_out.shape) != lead or not grad_out.is_contiguous():
+        raise ValueError("grad_out must be contiguous float32 with the targets shape")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != lead or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 with the targets shape")
+    dwt = hidden.dtype if dw_dtype is None else dw_dtype
+    d_hidden = torch.empty_like(hidden) if need_hidden else None
+    d_weight = torch.empty(weight.shape, dtype=dwt, device=dev) if need_weight else None
+    d_bias = torch.empty(V, dtype=torch.float32, device=dev) if need_bias else None
+    if workspace is None:
+        if workspace_bytes is None:
+            workspace_bytes = default_backward_workspace_bytes(N, D, V, hidden.dtype, dwt)
+        workspace = torch.empty(max(int(workspace_bytes), 16), dtype=torch.uint8, device=dev)
+    st = _abi.flp_backward(N, D, V, _X_DTYPES[hidden.dtype], _ptr(grad_out), _ptr(lse), _ptr(h2),
+                           _ptr(weight), _ptr(bias), _ptr(t1), _T_DTYPES[targets.dtype],
+                           _ptr(temp1), _ptr(d_hidden), _ptr(d_weight), _X_DTYPES[dwt],
+                           _ptr(d_bias), _ptr(workspace),
+                           workspace.numel() * workspace.element_size(), _stream(dev))
+    _check("flp_backward", st)
+    return d_hidden, d_weight, d_bias
+
+
+class LinearLogp(torch.autograd.Function):
+    """Autograd node: the forward saves lse; the backward recomputes the logits."""
+
+    @staticmethod
+    def forward(ctx, hidden, weight, targets, bias, temperature):
+        logp, lse = forward(hidden, weight, targets, bias, temperature, return_lse=True)
+        ctx.save_for_backward(hidden, weight, targets, bias, temperature, lse)
+        ctx.mark_non_differentiable(lse)
+        return logp, lse
+
+    @staticmethod
+    def backward(ctx, g_logp, g_lse):
+        hidden, weight, targets, bias, temperature, lse = ctx.saved_tensors
+        need_h, need_w, _, need_b, _ = ctx.needs_input_grad
+        if not (need_h or need_w or need_b):
+            return None, None, None, None, None
+        g = g_logp.contiguous().to(torch.float32)
+        dh, dw, db = backward(g, lse, hidden, weight, targets, bias, temperature,
+                              need_hidden=need_h, need_weight=need_w,
+                              need_bias=bool(need_b and bias is not None))
+        return dh, dw, None, db, None
+
+
+def linear_logp_with_lse(hidden, weight, targets, bias=None, temperature=None):
+    """(logp, lse): selected-token log-probabilities and the per-row log-sum-exp."""
+    return LinearLogp.apply(hidden, weight, targets, bias, temperature)
+
+
+def linear_logp(hidden, weight, targets, bias=None, temperature=None):
+    """logp[..] = log_softmax((hidden @ weight^T + bias) / T)[target], 0 for out-of-range targets."""
+    return linear_logp_with_lse(hidden, weight, targets, bias, temperature)[0]

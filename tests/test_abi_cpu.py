@@ -1,0 +1,140 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports every symbol
+include/flp.h declares, and its fail-closed gates reject bad arguments before
+any HIP call.  Pointers here are fake addresses: validation never dereferences
+them and every case returns before the device is touched."""
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flp.h")
+
+abi = pytest.importorskip("lm_head_selected_bf16_amd._abi")
+if not os.path.exists(abi.LIB_PATH):
+    pytest.skip("libflp.so not built (run __graft_entry__.build())", allow_module_level=True)
+
+lib = abi.load()
+S = {v: k for k, v in abi.STATUS_NAMES.items()}
+BF16, F32, I64, I32 = abi.FLP_BF16, abi.FLP_F32, abi.FLP_I64, abi.FLP_I32
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(flp_[a-z_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    names = header_functions()
+    assert set(names) == set(abi.SIGNATURES), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_build_info():
+    for code, name in abi.STATUS_NAMES.items():
+        assert abi.flp_status_string(code).startswith(name)
+    info = abi.flp_build_info()
+    assert "gfx950" in info and "vocab_tile=256" in info
+
+
+# fake, 16-byte aligned, non-overlapping device addresses
+H, W, B, T, TMP, LP, LS, WS = (0x10000000 * (k + 1) for k in range(8))
+N, D, V = 40, 64, 1000
+
+
+def fwd(**kw):
+    a = dict(N=N, D=D, V=V, x=BF16, hidden=H, weight=W, bias=B, targets=T, t=I64, temp=TMP,
+             logp=LP, lse=LS, ws=WS, wsb=abi.flp_forward_workspace_bytes(N, D, V), stream=0)
+    a.update(kw)
+    return abi.flp_forward(a["N"], a["D"], a["V"], a["x"], a["hidden"], a["weight"], a["bias"],
+                           a["targets"], a["t"], a["temp"], a["logp"], a["lse"], a["ws"], a["wsb"],
+                           a["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(N=-1), "FLP_INVALID_ARGUMENT"),
+    (dict(D=0), "FLP_INVALID_ARGUMENT"),
+    (dict(V=0), "FLP_INVALID_ARGUMENT"),
+    (dict(x=I64), "FLP_UNSUPPORTED_DTYPE"),
+    (dict(x=9), "FLP_UNSUPPORTED_DTYPE"),
+    (dict(t=BF16), "FLP_UNSUPPORTED_DTYPE"),
+    (dict(D=48), "FLP_UNSUPPORTED_SHAPE"),
+    (dict(N=2 ** 60), "FLP_UNSUPPORTED_SHAPE"),
+    (dict(hidden=0), "FLP_INVALID_ARGUMENT"),
+    (dict(weight=0), "FLP_INVALID_ARGUMENT"),
+    (dict(targets=0), "FLP_INVALID_ARGUMENT"),
+    (dict(logp=0), "FLP_INVALID_ARGUMENT"),
+    (dict(ws=0), "FLP_INVALID_ARGUMENT"),
+    (dict(hidden=H + 8), "FLP_MISALIGNED"),
+    (dict(weight=W + 4), "FLP_MISALIGNED"),
+    (dict(logp=LP + 2), "FLP_MISALIGNED"),
+    (dict(targets=T + 4), "FLP_MISALIGNED"),
+    (dict(ws=WS + 8), "FLP_MISALIGNED"),
+    (dict(logp=H + 64), "FLP_INVALID_ARGUMENT"),          # output inside hidden
+    (dict(lse=LP + 16), "FLP_INVALID_ARGUMENT"),          # two outputs overlap
+    (dict(ws=W + 1024), "FLP_INVALID_ARGUMENT"),          # workspace inside weight
+    (dict(wsb=100), "FLP_WORKSPACE_TOO_SMALL"),
+    (dict(N=0, hidden=0, targets=0, logp=0, ws=0), "FLP_OK"),   # empty batch: no-op
+])
+def test_forward_gates(kw, expect):
+    assert abi.STATUS_NAMES[fwd(**kw)] == expect
+
+
+def bwd(**kw):
+    a = dict(N=N, D=D, V=V, x=BF16, g=TMP, lse=LS, hidden=H, weight=W, bias=B, targets=T, t=I64,
+             temp=0, dh=0x90000000, dw=0xA0000000, dwt=BF16, db=0xB0000000, ws=WS,
+             wsb=abi.flp_backward_workspace_bytes(N, D, V, BF16, BF16, 0), stream=0)
+    a.update(kw)
+    return abi.flp_backward(a["N"], a["D"], a["V"], a["x"], a["g"], a["lse"], a["hidden"],
+                            a["weight"], a["bias"], a["targets"], a["t"], a["temp"], a["dh"],
+                            a["dw"], a["dwt"], a["db"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(N=-3), "FLP_INVALID_ARGUMENT"),
+    (dict(x=F32, dwt=BF16), "FLP_UNSUPPORTED_DTYPE"),   # d_weight dtype must be x or f32
+    (dict(dwt=I32), "FLP_UNSUPPORTED_DTYPE"),
+    (dict(D=100), "FLP_UNSUPPORTED_SHAPE"),
+    (dict(g=0), "FLP_INVALID_ARGUMENT"),
+    (dict(lse=0), "FLP_INVALID_ARGUMENT"),
+    (dict(ws=0), "FLP_INVALID_ARGUMENT"),
+    (dict(dh=0x90000002), "FLP_MISALIGNED"),
+    (dict(db=0xB0000002), "FLP_MISALIGNED"),
+    (dict(dh=H), "FLP_INVALID_ARGUMENT"),               # d_hidden aliases hidden
+    (dict(db=0xA0000000 + 64), "FLP_INVALID_ARGUMENT"), # d_bias inside d_weight
+    (dict(wsb=1000), "FLP_WORKSPACE_TOO_SMALL"),
+    (dict(dh=0, dw=0, db=0, ws=0), "FLP_OK"),           # nothing requested: no-op
+    (dict(N=0, g=0, lse=0, hidden=0, targets=0, ws=0), "FLP_OK"),
+])
+def test_backward_gates(kw, expect):
+    assert abi.STATUS_NAMES[bwd(**kw)] == expect
+
+
+def test_workspace_sizes():
+    # forward: one (max, sum) pair per row and 256-column vocabulary tile + the target logits
+    n_vt = -(-V // 256)
+    fb = abi.flp_forward_workspace_bytes(N, D, V)
+    assert fb >= n_vt * N * 8 + N * 4 and fb % 256 == 0
+    assert abi.flp_forward_workspace_bytes(-1, D, V) == 0
+    # backward: the minimum is a 256-row chunk; bigger chunks cost more
+    lo = abi.flp_backward_workspace_bytes(5000, 2688, 131072, BF16, BF16, 0)
+    hi = abi.flp_backward_workspace_bytes(5000, 2688, 131072, BF16, BF16, 5000)
+    assert 0 < lo < hi
+    # a single chunk needs no fp32 d_weight accumulator
+    one = abi.flp_backward_workspace_bytes(256, 2688, 131072, BF16, BF16, 256)
+    assert one < 131072 * 2688 * 4
+    # several chunks with a bf16 d_weight need the fp32 accumulator
+    assert lo > 131072 * 2688 * 4
+    # chunk rows round up to multiples of 256 and are capped at N
+    assert (abi.flp_backward_workspace_bytes(600, 64, 1000, BF16, BF16, 300) ==
+            abi.flp_backward_workspace_bytes(600, 64, 1000, BF16, BF16, 512))
+    assert (abi.flp_backward_workspace_bytes(600, 64, 1000, BF16, BF16, 10 ** 6) ==
+            abi.flp_backward_workspace_bytes(600, 64, 1000, BF16, BF16, 768))
+
+
+def test_workspace_below_minimum_rejected():
+    lo = abi.flp_backward_workspace_bytes(N, D, V, BF16, BF16, 0)
+    for short in (1, 255, 4096, lo - 1):
+        assert abi.STATUS_NAMES[bwd(wsb=short)] == "FLP_WORKSPACE_TOO_SMALL"

@@ -1,0 +1,114 @@
+"""Bitwise batch invariance and determinism of the HIP path (PR #555,
+"Acceptance checks": batch sizes 1/2/7/64/255/257 on random row subsets, a
+[3, 100] leading shape, repeat runs, train vs rollout entry, grad_hidden rows at
+1/7/64/257; chunking of the backward is bit-neutral)."""
+import numpy as np
+import pytest
+import torch
+
+import flp_inputs
+from gpu_common import flp, gpu_backward, gpu_forward, inputs, say, to_gpu
+
+pytestmark = pytest.mark.gpu
+BF16 = torch.bfloat16
+
+
+@pytest.fixture(scope="module")
+def rollout():
+    inp = inputs("rollout_n8192")
+    g = to_gpu(inp)
+    logp, lse = gpu_forward(g)
+    return inp, g, logp, lse
+
+
+def _subset(g, rows):
+    idx = torch.as_tensor(rows, device=g["hidden"].device)
+    sub = dict(g)
+    for k in ("hidden", "targets", "temperature", "grad_out"):
+        if g.get(k) is not None:
+            sub[k] = g[k][idx].contiguous()
+    return sub
+
+
+@pytest.mark.parametrize("n", [1, 2, 7, 64, 255, 257, 4096])
+def test_forward_row_subsets(rollout, n):
+    """A row's logp and lse do not depend on the other rows or on N (different N
+    select different row-tile kernels)."""
+    inp, g, logp, lse = rollout
+    rows = flp_inputs.random_rows(8192, n, seed=1000 + n).numpy()
+    rows = np.random.default_rng(n).permutation(rows)  # also scramble the order
+    lp, ls = gpu_forward(_subset(g, rows))
+    say(f"subset n={n}")
+    assert torch.equal(lp, logp[rows]) and torch.equal(ls, lse[rows])
+
+
+def test_forward_leading_shape(rollout):
+    inp, g, logp, lse = rollout
+    rows = flp_inputs.random_rows(8192, 300, seed=7).numpy()
+    sub = _subset(g, rows)
+    sub3 = {k: (v.reshape(3, 100, *v.shape[1:]) if k in ("hidden", "targets", "temperature")
+                else v) for k, v in sub.items()}
+    lp, ls = gpu_forward(sub3)
+    assert lp.shape == (3, 100)
+    assert torch.equal(lp.reshape(-1), logp[rows]) and torch.equal(ls.reshape(-1), lse[rows])
+
+
+def test_forward_repeat_and_rollout_entry(rollout):
+    inp, g, logp, lse = rollout
+    lp2, ls2 = gpu_forward(g)
+    lp3, none = gpu_forward(g, return_lse=False)
+    assert none is None
+    assert torch.equal(lp2, logp) and torch.equal(ls2, lse) and torch.equal(lp3, logp)
+
+
+def test_int32_targets_same_bits(rollout):
+    inp, g, logp, lse = rollout
+    g32 = dict(g)
+    g32["targets"] = g["targets"].to(torch.int32)
+    lp, ls = gpu_forward(g32)
+    assert torch.equal(lp, logp) and torch.equal(ls, lse)
+
+
+@pytest.fixture(scope="module")
+def train_small():
+    inp = inputs("train_n16384", n_rows=1100)
+    g = to_gpu(inp)
+    logp, lse = gpu_forward(g)
+    return inp, g, logp, lse
+
+
+@pytest.mark.parametrize("n", [1, 7, 64, 257])
+def test_d_hidden_row_subsets(train_small, n):
+    inp, g, logp, lse = train_small
+    dh, _, _ = gpu_backward(g, lse, need_weight=False, need_bias=False)
+    rows = flp_inputs.random_rows(1100, n, seed=2000 + n).numpy()
+    sub = _subset(g, rows)
+    lp_s, lse_s = gpu_forward(sub)
+    assert torch.equal(lse_s, lse[rows])
+    dh_s, _, _ = gpu_backward(sub, lse_s, need_weight=False, need_bias=False)
+    say(f"d_hidden subset n={n}")
+    assert torch.equal(dh_s, dh[rows])
+
+
+def test_backward_chunking_is_bit_neutral(train_small):
+    """256-row chunks (fp32 d_weight accumulator across chunks) vs one chunk."""
+    inp, g, logp, lse = train_small
+    m = flp()
+    N, D, V = 1100, 2688, 131072
+    one = gpu_backward(g, lse, need_bias=True,
+                       workspace_bytes=m.backward_workspace_bytes(N, D, V, BF16, chunk_rows=N))
+    many = gpu_backward(g, lse, need_bias=True,
+                        workspace_bytes=m.backward_workspace_bytes(N, D, V, BF16, chunk_rows=256))
+    mid = gpu_backward(g, lse, need_bias=True,
+                       workspace_bytes=m.backward_workspace_bytes(N, D, V, BF16, chunk_rows=512))
+    for name, a, b, c in zip(("d_hidden", "d_weight", "d_bias"), one, many, mid):
+        say(f"chunking {name}")
+        assert torch.equal(a, b) and torch.equal(a, c), name
+    # the same with an fp32 d_weight output (accumulates in the caller's buffer)
+    f1 = gpu_backward(g, lse, need_bias=False, dw_dtype=torch.float32,
+                      workspace_bytes=m.backward_workspace_bytes(N, D, V, BF16, torch.float32, N))
+    f2 = gpu_backward(g, lse, need_bias=False, dw_dtype=torch.float32,
+                      workspace_bytes=m.backward_workspace_bytes(N, D, V, BF16, torch.float32, 256))
+    assert torch.equal(f1[1], f2[1])
+    # bf16 d_weight is the single rounding of the fp32 one
+    assert torch.equal(f1[1].to(BF16), one[1])

@@ -1,0 +1,176 @@
+"""HIP path vs the CPU FP64 oracle, element by element, through the C ABI.
+
+Small cases (several tiles and ragged tails in every dimension) are compared on
+every output.  The full-size workloads run in the launch configuration the
+benchmark uses and are compared on sampled rows the oracle computes one by one;
+d_weight / d_bias at full size use a grad_out that is non-zero on sampled rows
+only (every other row then contributes exactly zero), plus properties that hold
+at any size."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import flp_inputs
+from gpu_common import (FP32_CELL, LOGP_CELL, REDUCTION_CELL, check_close, flp, gpu_backward,
+                        gpu_forward, inputs, oracle_backward, oracle_forward, say, to_gpu)
+
+pytestmark = pytest.mark.gpu
+
+BF16 = torch.bfloat16
+
+
+def cells(dtype):
+    return (FP32_CELL, FP32_CELL) if dtype == torch.float32 else (LOGP_CELL, REDUCTION_CELL)
+
+
+def full_check(inp, g, dtype, dw_dtype=None):
+    lc, rc = cells(dtype)
+    logp, lse = gpu_forward(g)
+    rl, rs = oracle_forward(inp)
+    check_close("logp", logp, rl, **lc)
+    check_close("lse", lse, rs, **lc)
+    dh, dw, db = gpu_backward(g, lse, dw_dtype=dw_dtype, need_bias=True)
+    odh, odw, odb = oracle_backward(inp)
+    check_close("d_hidden", dh, odh, **lc)
+    check_close("d_weight", dw, odw, **rc)
+    check_close("d_bias", db, odb, **rc)
+    # ignored rows: logp exactly 0 and a zero gradient row
+    t = inp["targets"].numpy()
+    ign = (t < 0) | (t >= inp["workload"].V)
+    if ign.any():
+        assert np.all(logp.cpu().numpy()[ign] == 0.0)
+        assert np.all(dh.float().cpu().numpy()[ign] == 0.0)
+
+
+def test_tiny_fp32_fwd_bwd():
+    """The tiny fp32 workload (N=64, D=256, V=4096, 4 ignored rows), every output."""
+    say("case tiny_fp32: N=64 D=256 V=4096 fp32")
+    inp = inputs("tiny_fp32")
+    full_check(inp, to_gpu(inp), torch.float32)
+
+
+SMALL = [
+    # (dtype, N, D, V, bias_std, temperature, t_dtype, n_ignored)
+    (BF16, 300, 512, 4133, 0.1, (0.5, 1.5), torch.int32, 7),
+    (BF16, 77, 96, 1000, None, (0.7, 1.3), torch.int64, 3),
+    (torch.float32, 300, 96, 4133, 0.1, None, torch.int64, 5),
+    (BF16, 513, 2688, 2048, 0.1, (0.5, 1.5), torch.int64, 9),
+    (BF16, 1, 64, 300, None, None, torch.int64, 0),
+]
+
+
+def small_inputs(case, k):
+    dtype, N, D, V, bstd, temp, tdt, nign = case
+    w = flp_inputs.Workload(f"small{k}", 100 + k, N, D, V, dtype, w_std=1.0 / np.sqrt(D) * 1.3,
+                            bias_std=bstd, n_ignored=nign,
+                            ignore_values=(-1, V, -7, V + 3), temperature=temp,
+                            grad="normal", leading=(N,))
+    inp = flp_inputs.make_inputs(w)
+    inp["targets"] = inp["targets"].to(tdt)
+    return inp
+
+
+@pytest.mark.parametrize("k", range(len(SMALL)))
+def test_small_ragged(k):
+    case = SMALL[k]
+    say(f"case small{k}: {case}")
+    inp = small_inputs(case, k)
+    full_check(inp, to_gpu(inp), case[0])
+
+
+def test_small_bf16_fp32_dweight():
+    """bf16 inputs with an fp32 d_weight output (one rounding less)."""
+    inp = small_inputs(SMALL[0], 0)
+    say("case small0 with fp32 d_weight")
+    full_check(inp, to_gpu(inp), BF16, dw_dtype=torch.float32)
+
+
+def test_decode_n32_full():
+    """Decode-scale forward at its full size: all 32 rows against the oracle."""
+    say("case decode_n32: N=32 D=2688 V=131072 bf16, forward")
+    inp = inputs("decode_n32")
+    g = to_gpu(inp)
+    logp, lse = gpu_forward(g)
+    rl, rs = oracle_forward(inp)
+    check_close("logp", logp.reshape(-1), rl, **LOGP_CELL)
+    check_close("lse", lse.reshape(-1), rs, **LOGP_CELL)
+
+
+def test_rollout_n8192_sampled():
+    """Rollout-scale forward with temperature: 48 sampled rows of the full launch."""
+    say("case rollout_n8192: N=8192 D=2688 V=131072 bf16 + temperature, forward")
+    inp = inputs("rollout_n8192")
+    g = to_gpu(inp)
+    logp, lse = gpu_forward(g)
+    rows = flp_inputs.random_rows(8192, 48, seed=31).numpy()
+    rl, rs = oracle_forward(inp, rows=rows)
+    check_close("logp[rows]", logp.reshape(-1)[rows], rl, **LOGP_CELL)
+    check_close("lse[rows]", lse.reshape(-1)[rows], rs, **LOGP_CELL)
+
+
+def _sparse_grad(inp, rows):
+    go = torch.zeros_like(inp["grad_out"])
+    go[rows] = inp["grad_out"][rows]
+    return go
+
+
+def _train_like(name, n_sample, ws_bytes=None):
+    inp = inputs(name)
+    g = to_gpu(inp)
+    N = inp["workload"].N
+    logp, lse = gpu_forward(g)
+    rows = flp_inputs.random_rows(N, n_sample, seed=41).numpy()
+    rl, rs = oracle_forward(inp, rows=rows)
+    check_close("logp[rows]", logp[rows], rl, **LOGP_CELL)
+    check_close("lse[rows]", lse[rows], rs, **LOGP_CELL)
+    t = inp["targets"].numpy()
+    ign = (t < 0) | (t >= inp["workload"].V)
+    assert np.all(logp.cpu().numpy()[ign] == 0.0)
+
+    # dense grad_out: d_hidden rows are per-row, so the oracle computes the sampled ones
+    dh, dw, db = gpu_backward(g, lse, need_bias=True, workspace_bytes=ws_bytes)
+    odh, _, _ = oracle_backward(inp, rows=rows, need_weight=False, need_bias=False)
+    check_close("d_hidden[rows]", dh[rows], odh, **LOGP_CELL)
+    assert np.all(dh.float().cpu().numpy()[ign] == 0.0)
+    # Every valid row's dlogits sums to zero over the vocabulary, up to the fp32
+    # rounding of its lse: sum_v exp(z - lse^) = exp(lse - lse^) with
+    # |lse - lse^| <= (|lse| + 1) 2^-21 (a few roundings of the sum, the log and
+    # the add), which is below 1e-5 at these logit scales; the errors of a row
+    # share one sign, so the bound adds them over rows.
+    G = np.abs(inp["grad_out"].numpy())
+    G[ign] = 0.0
+    bound = 1e-5 * float(G.sum()) + 1e-3
+    tot = float(db.double().sum())
+    say(f"  sum_v d_bias = {tot:.3e} (bound {bound:.3e})")
+    assert abs(tot) < bound
+    # bitwise determinism: a second run
+    dh2, dw2, db2 = gpu_backward(g, lse, need_bias=True, workspace_bytes=ws_bytes)
+    assert torch.equal(dh, dh2) and torch.equal(dw, dw2) and torch.equal(db, db2)
+    del dh2, dw2, db2
+
+    # sparse grad_out: the oracle's d_weight / d_bias over the sampled rows are the full answer
+    go = _sparse_grad(inp, rows)
+    sdh, sdw, sdb = gpu_backward(g, lse, grad_out=go.to(g["hidden"].device), need_bias=True,
+                                 workspace_bytes=ws_bytes)
+    odh, odw, odb = oracle_backward(inp, grad_out=go, rows=rows)
+    check_close("sparse d_weight", sdw, odw, **REDUCTION_CELL)
+    check_close("sparse d_bias", sdb, odb, **REDUCTION_CELL)
+    check_close("sparse d_hidden[rows]", sdh[rows], odh, **LOGP_CELL)
+    others = np.setdiff1d(np.arange(N), rows)
+    assert torch.count_nonzero(sdh[torch.as_tensor(others, device=sdh.device)]) == 0
+
+
+def test_train_n16384():
+    say("case train_n16384: N=16384 D=2688 V=131072 bf16, bias, fwd+bwd")
+    _train_like("train_n16384", 32)
+
+
+def test_longseq_n65600_multichunk():
+    """N=65600 with 5% out-of-range targets, backward in several row chunks (the
+    fp32 d_weight accumulator path)."""
+    say("case longseq_n65600: N=65600 D=2688 V=131072 bf16, fwd+bwd, 16384-row chunks")
+    m = flp()
+    ws = m.backward_workspace_bytes(65600, 2688, 131072, BF16, chunk_rows=16384)
+    _train_like("longseq_n65600", 24, ws_bytes=ws)
