@@ -1,0 +1,322 @@
+#!/usr/bin/env python3
+"""Throughput of the fused linear selected-token log-prob on one MI355X.
+
+One step = flp_forward + flp_backward (logp, lse, d_hidden, d_weight, d_bias)
+over the training workload N = 16384 tokens (B = 4, S = 4096), D = 2688,
+V = 131072, bf16 hidden/W, fp32 bias, grad_out ~ N(0, 1); d_weight in bf16
+from fp32 accumulation.  Inputs are synthetic (seeded; see flp_inputs.py) and
+resident in HBM before the timed region; outputs and workspaces are
+preallocated.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Roofline: per-kernel durations come from HIP events the library records around
+each of its launches during the timed steps (flp_profile_*); the dominant
+kernel's algorithmic flops per launch (2 N D V for a full-batch launch of any
+of the four contractions) over its mean duration, against the bf16 dense MFMA
+peak.  cpu_baseline: the CPU FP64 oracle, as it stands, on a bounded sample of
+rows of the same workload, scaled to tokens/s.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+# The pages' own number for this exact workload on other hardware (H100 PCIe,
+# strict deterministic path, cuBLASLt no-split-K): 351.2 ms per fwd+bwd at 16384 tokens.
+PAGES_STRICT_TOK_S = 16384 / 0.3512
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    p = os.path.join(ROOT, "lm_head_selected_bf16_amd", "csrc", "flp_kernels.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it was
+    taken on the current kernel source (else None)."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except Exception:  # noqa: BLE001
+        return None
+    if d.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    k = d.get("kernels", {}).get(kernel)
+    if not k:
+        return None
+    return k.get("hbm_bytes_per_launch")
+
+
+class Problem:
+    """Device buffers of one workload and raw C-ABI calls over them."""
+
+    def __init__(self, name: str, backward: bool):
+        import torch
+
+        import flp_inputs
+        import lm_head_selected_bf16_amd as m
+
+        self.m = m
+        self.torch = torch
+        inp = flp_inputs.make_inputs(name)
+        self.cpu = inp
+        w = inp["workload"]
+        self.w = w
+        self.N, self.D, self.V = w.N, w.D, w.V
+        dev = "cuda:0"
+        g = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+        self.g = g
+        self.x = m.FLP_BF16 if w.dtype == torch.bfloat16 else m.FLP_F32
+        self.logp = torch.empty(self.N, device=dev)
+        self.lse = torch.empty(self.N, device=dev)
+        fb = m.flp_forward_workspace_bytes(self.N, self.D, self.V)
+        self.fws = torch.empty(fb, dtype=torch.uint8, device=dev)
+        self.backward = backward
+        if backward:
+            self.dh = torch.empty_like(g["hidden"])
+            self.dw = torch.empty_like(g["weight"])
+            self.db = torch.empty(self.V, device=dev)
+            bb = m.default_backward_workspace_bytes(self.N, self.D, self.V, w.dtype)
+            self.bws = torch.empty(bb, dtype=torch.uint8, device=dev)
+        self.stream = torch.cuda.current_stream().cuda_stream
+
+    def p(self, t):
+        return 0 if t is None else int(t.data_ptr())
+
+    def forward(self):
+        g, m = self.g, self.m
+        st = m.flp_forward(self.N, self.D, self.V, self.x, self.p(g["hidden"]), self.p(g["weight"]),
+                           self.p(g["bias"]), self.p(g["targets"]), m.FLP_I64,
+                           self.p(g["temperature"]), self.p(self.logp), self.p(self.lse),
+                           self.p(self.fws), self.fws.numel(), self.stream)
+        if st != m.FLP_OK:
+            raise m.FlpError("flp_forward", st)
+
+    def step(self):
+        self.forward()
+        if not self.backward:
+            return
+        g, m = self.g, self.m
+        st = m.flp_backward(self.N, self.D, self.V, self.x, self.p(g["grad_out"]), self.p(self.lse),
+                            self.p(g["hidden"]), self.p(g["weight"]), self.p(g["bias"]),
+                            self.p(g["targets"]), m.FLP_I64, self.p(g["temperature"]),
+                            self.p(self.dh), self.p(self.dw), self.x, self.p(self.db),
+                            self.p(self.bws), self.bws.numel(), self.stream)
+        if st != m.FLP_OK:
+            raise m.FlpError("flp_backward", st)
+
+    def time_steps(self, steps: int, warmup: int):
+        torch, m = self.torch, self.m
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        m.flp_profile_read()          # drop anything recorded before
+        m.flp_profile_enable(True)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(steps):
+            self.step()
+        e1.record()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        m.flp_profile_enable(False)
+        prof = m.flp_profile_read()
+        return (t1 - t0) * 1e3 / steps, e0.elapsed_time(e1) / steps, prof
+
+
+def contraction_flops(kind: str, N: int, D: int, V: int, launches_per_step: int) -> float:
+    """Algorithmic flops per launch of a contraction kernel (rows split evenly
+    over the launches of one step)."""
+    if kind in ("forward", "dlogits", "d_hidden", "d_weight"):
+        return 2.0 * N * D * V / launches_per_step
+    return 0.0
+
+
+def cpu_baseline(prob: Problem, target_s: float = 15.0):
+    """The oracle on a bounded sample of rows: fwd + bwd (d_hidden, d_weight, d_bias)."""
+    import numpy as np
+    import threadpoolctl
+
+    import flp_inputs
+    import oracle
+
+    inp = prob.cpu
+    H = oracle.as_f64(inp["hidden"])
+    W = oracle.as_f64(inp["weight"])          # up-cast once, outside the timed region
+    b = oracle.as_f64(inp["bias"])
+    T = oracle.as_f64(inp["temperature"])
+    t = inp["targets"].numpy()
+    g = inp["grad_out"].numpy()
+    info = [i for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+
+    def run(rows):
+        t0 = time.perf_counter()
+        oracle.forward(H, W, t, b, T, rows=rows)
+        oracle.backward(H, W, t, g, b, T, rows=rows)
+        return time.perf_counter() - t0
+
+    # At least one whole 512-row chunk of the oracle: its d_weight update over
+    # V x D is a fixed cost per chunk that a smaller sample would not amortise.
+    probe = flp_inputs.random_rows(prob.N, 512, seed=5).numpy()
+    dt = run(probe)
+    n = int(min(2048, max(512, 512 * target_s / max(dt, 1e-3))))
+    n -= n % 512
+    if n > 512:
+        log(f"cpu baseline: 512 rows took {dt:.2f}s -> timing {n} rows")
+        rows = flp_inputs.random_rows(prob.N, n, seed=6).numpy()
+        dt = run(rows)
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} random rows of the {prob.w.name} workload (D={prob.D}, V={prob.V}), "
+                      f"fwd + bwd (logp, lse, d_hidden, d_weight, d_bias) in float64 numpy, "
+                      f"{dt:.1f} s; scaled to tokens/s (the oracle's work is linear in rows)",
+            "host_cpus": os.cpu_count(), "affinity": len(os.sched_getaffinity(0))}
+
+
+def forward_only(name: str, steps: int, warmup: int, bound: str):
+    prob = Problem(name, backward=False)
+    ms, ems, prof = prob.time_steps(steps, warmup)
+    fwd_ms, fwd_n = prof["forward"]
+    k_ms = fwd_ms / max(fwd_n, 1)
+    out = {"workload": name, "N": prob.N, "ms_per_call": round(ms, 4),
+           "tokens_per_s": round(prob.N / (ms / 1e3), 1), "forward_kernel_ms": round(k_ms, 4),
+           "merge_kernel_ms": round(prof["merge"][0] / max(prof["merge"][1], 1), 4)}
+    if bound == "hbm":
+        # algorithmic bytes: W + hidden read once, targets read, logp + lse written
+        byts = prob.V * prob.D * 2 + prob.N * prob.D * 2 + prob.N * 8 + prob.N * 8
+        out.update(bound="hbm", algorithmic_bytes=byts,
+                   achieved_GBs=round(byts / (k_ms / 1e3) / 1e9, 1), peak_GBs=PEAK_HBM_GBS,
+                   frac=round(byts / (k_ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4))
+    else:
+        fl = 2.0 * prob.N * prob.D * prob.V
+        out.update(bound="mfma", algorithmic_flops=fl,
+                   achieved_TFLOPs=round(fl / (k_ms / 1e3) / 1e12, 1), peak_TFLOPs=PEAK_BF16_TFLOPS,
+                   frac=round(fl / (k_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4))
+    del prob
+    return out
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the forward-only decode (N=32) and rollout (N=8192) figures")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 3 times (reference for "
+                         "the FETCH_SIZE / WRITE_SIZE counters)")
+    args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": n}), flush=True)
+        return 0
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+    import lm_head_selected_bf16_amd as m
+
+    m.load()
+    torch.cuda.set_device(0)
+    log(m.flp_build_info())
+    name = "train_n16384"
+    log(f"preparing {name}")
+    prob = Problem(name, backward=True)
+    N, D, V = prob.N, prob.D, prob.V
+    log(f"warmup {args.warmup}, timing {args.steps} steps")
+    ms, ems, prof = prob.time_steps(args.steps, args.warmup)
+    log(f"{ms:.3f} ms/step (events {ems:.3f})")
+
+    kernels = {}
+    for kind, (tot, n) in prof.items():
+        if n == 0:
+            continue
+        per_step = n / args.steps
+        fl = contraction_flops(kind, N, D, V, int(round(per_step)))
+        avg = tot / n
+        kernels[kind] = {"ms_per_launch": round(avg, 4), "launches_per_step": per_step,
+                         "ms_per_step": round(tot / args.steps, 4)}
+        if fl:
+            kernels[kind]["TFLOPs"] = round(fl / (avg / 1e3) / 1e12, 1)
+    dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    dom_n = int(round(kernels[dom]["launches_per_step"]))
+    dom_fl = contraction_flops(dom, N, D, V, dom_n)
+    dom_avg_s = kernels[dom]["ms_per_launch"] / 1e3
+    achieved = dom_fl / dom_avg_s / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": load_traffic(name, dom),
+                "algorithmic_flops_per_launch": dom_fl}
+    step_flops = 8.0 * N * D * V
+    value = N / (ms / 1e3)
+    out = {
+        "metric": "fwd+bwd tokens/s at D=2688,V=131072 bf16; % of MFMA / HBM roofline",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": round(value / PAGES_STRICT_TOK_S, 3),
+        "baseline_note": "vs the pages' strict deterministic fwd+bwd at 16384 tokens on H100 PCIe "
+                         "(351.2 ms); other hardware, context only",
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "train_n16384: fwd+bwd, N=16384 tokens (B=4, S=4096), D=2688, "
+                               "V=131072, bf16 hidden/W, fp32 bias, grad_out~N(0,1), bf16 d_W "
+                               "with fp32 accumulation, single 16384-row backward chunk",
+                   "N": N, "D": D, "V": V, "global_batch": 4, "seq_len": 4096,
+                   "parallelism": "single GPU"},
+        "method_TFLOPs": round(step_flops / (ms / 1e3) / 1e12, 1),
+        "method_frac_of_peak": round(step_flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+    del prob
+    torch.cuda.empty_cache()
+    if not args.no_extra:
+        log("forward-only: decode_n32")
+        out["decode_n32_forward"] = forward_only("decode_n32", 50, 10, "hbm")
+        log("forward-only: rollout_n8192")
+        out["rollout_n8192_forward"] = forward_only("rollout_n8192", 10, 3, "mfma")
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        cpu_prob = Problem.__new__(Problem)
+        import flp_inputs
+        cpu_prob.cpu = flp_inputs.make_inputs(name)
+        cpu_prob.w = cpu_prob.cpu["workload"]
+        cpu_prob.N, cpu_prob.D, cpu_prob.V = cpu_prob.w.N, cpu_prob.w.D, cpu_prob.w.V
+        out["cpu_baseline"] = cpu_baseline(cpu_prob)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -20,8 +20,10 @@
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers on the current HIP device,
  *     row-major and densely packed, owned by the caller.  The library
- *     allocates nothing and keeps no state besides a once-initialised
- *     per-device property cache; the calls are re-entrant.
+ *     allocates no device memory and keeps no state besides a once-
+ *     initialised per-device property cache (and, only while the optional
+ *     kernel timing below is enabled, a pool of HIP events); the calls are
+ *     re-entrant.
  *   - Work is enqueued on `stream` (a hipStream_t, or NULL for the default
  *     stream) and the call returns at once.  Outputs are valid once the
  *     stream has synchronised; device faults surface there.
@@ -138,6 +140,31 @@ flp_status flp_backward(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
                         void* d_hidden, void* d_weight, flp_dtype dw_dtype,
                         float* d_bias,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Optional per-kernel timing with HIP events, for benchmarks.  While enabled,
+ * every kernel the library enqueues is bracketed by two events recorded on
+ * the same stream; flp_profile_read synchronises those events and returns, per
+ * kernel kind, the summed duration in milliseconds and the launch count since
+ * the previous read (then clears them).  Enabling it adds two event records
+ * per kernel and nothing else; results are unaffected.  Process-wide, guarded
+ * by a mutex.
+ */
+typedef enum flp_kernel_kind {
+  FLP_K_FORWARD = 0,    /* logits tile + per-tile (max, sum of exp) + target logit */
+  FLP_K_MERGE = 1,      /* ascending fold of the tile partials -> lse, logp */
+  FLP_K_DLOGITS = 2,    /* logits tile recompute -> dz, dz^T, d_bias partials */
+  FLP_K_TRANSPOSE = 3,  /* hidden chunk -> hidden^T */
+  FLP_K_DHIDDEN = 4,    /* d_hidden = dz W */
+  FLP_K_DWEIGHT = 5,    /* d_weight (+)= dz^T hidden */
+  FLP_K_DBIAS = 6,      /* ascending fold of the d_bias partials */
+  FLP_K_COUNT = 7
+} flp_kernel_kind;
+
+void flp_profile_enable(int on);
+/* ms[k] and count[k] for k < min(n, FLP_K_COUNT); returns FLP_HIP_ERROR if an
+ * event query fails. */
+flp_status flp_profile_read(double* ms, int64_t* count, int n);
 
 /* Static text for a status code. */
 const char* flp_status_string(flp_status status);

@@ -36,6 +36,8 @@ SIGNATURES = {
     "flp_backward_workspace_bytes": (_sz, [_i64, _i64, _i64, _int, _int, _i64]),
     "flp_backward": (_int, [_i64, _i64, _i64, _int, _fp, _fp, _vp, _vp, _fp, _vp, _int, _fp, _vp,
                             _vp, _int, _fp, _vp, _sz, _vp]),
+    "flp_profile_enable": (None, [_int]),
+    "flp_profile_read": (_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64), _int]),
     "flp_status_string": (ctypes.c_char_p, [_int]),
     "flp_build_info": (ctypes.c_char_p, []),
 }
@@ -100,6 +102,24 @@ def flp_backward(N, D, V, x_dtype, grad_out, lse, hidden, weight, bias, targets,
     return int(load().flp_backward(N, D, V, x_dtype, grad_out, lse, hidden, weight, bias, targets,
                                    t_dtype, temperature, d_hidden, d_weight, dw_dtype, d_bias,
                                    workspace, workspace_bytes, stream))
+
+
+KERNEL_KINDS = ("forward", "merge", "dlogits", "transpose", "d_hidden", "d_weight", "d_bias")
+
+
+def flp_profile_enable(on: bool) -> None:
+    load().flp_profile_enable(1 if on else 0)
+
+
+def flp_profile_read() -> dict:
+    """{kind: (total_ms, launches)} since the previous read."""
+    n = len(KERNEL_KINDS)
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int64 * n)()
+    st = int(load().flp_profile_read(ms, cnt, n))
+    if st != FLP_OK:
+        raise FlpError("flp_profile_read", st)
+    return {k: (float(ms[i]), int(cnt[i])) for i, k in enumerate(KERNEL_KINDS)}
 
 
 def flp_status_string(status: int) -> str:

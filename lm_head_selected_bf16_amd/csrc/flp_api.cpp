@@ -5,7 +5,9 @@
 #include <atomic>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "flp_launch.h"
 
@@ -33,7 +35,54 @@ flp_status check_device() {
 
 inline char* at(void* base, size_t off) { return static_cast<char*>(base) + off; }
 
+// ---- optional per-kernel event timing ----
+struct ProfRec {
+  int kind;
+  hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+std::atomic<bool> g_prof_on{false};
+std::vector<ProfRec> g_prof_recs;
+std::vector<hipEvent_t> g_prof_pool;
+
+hipEvent_t prof_event() {
+  if (!g_prof_pool.empty()) {
+    hipEvent_t e = g_prof_pool.back();
+    g_prof_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
 }  // namespace
+
+namespace flp {
+
+ProfScope::ProfScope(int k, hipStream_t s) : kind(k), stream(s) {
+  if (!g_prof_on.load(std::memory_order_relaxed)) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  a = prof_event();
+  if (a != nullptr && hipEventRecord(a, stream) != hipSuccess) {
+    g_prof_pool.push_back(a);
+    a = nullptr;
+  }
+}
+
+ProfScope::~ProfScope() {
+  if (a == nullptr) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  hipEvent_t b = prof_event();
+  if (b == nullptr || hipEventRecord(b, stream) != hipSuccess) {
+    g_prof_pool.push_back(a);
+    if (b != nullptr) g_prof_pool.push_back(b);
+    return;
+  }
+  g_prof_recs.push_back(ProfRec{kind, a, b});
+}
+
+}  // namespace flp
 
 extern "C" {
 
@@ -107,6 +156,10 @@ flp_status flp_backward(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
   const size_t xs = dtype_size(x_dtype);
   const size_t ts = dtype_size(t_dtype);
   void* dz = d_hidden ? at(workspace, L.dz_off) : nullptr;
+  void* wT = d_hidden ? at(workspace, L.wt_off) : nullptr;
+  if (d_hidden &&
+      launch_transpose(x_dtype, weight, V, L.ldz, D, D, wT, L.ldz, s) != hipSuccess)
+    return FLP_HIP_ERROR;
   void* dzT = d_weight ? at(workspace, L.dzt_off) : nullptr;
   void* hT = d_weight ? at(workspace, L.ht_off) : nullptr;
   float* dbp = d_bias ? reinterpret_cast<float*>(at(workspace, L.dbp_off)) : nullptr;
@@ -143,12 +196,12 @@ flp_status flp_backward(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
     if (d_hidden) {
       GemmArgs g;
       g.a = dz;
-      g.b = weight;
+      g.b = wT;
       g.lda_b = L.ldz * int64_t(xs);
-      g.ldb_b = D * int64_t(xs);
+      g.ldb_b = L.ldz * int64_t(xs);
       g.M = rows;
       g.N = D;
-      g.K = V;
+      g.K = L.ldz;  // dz and W^T are zero past V
       g.out = static_cast<char*>(d_hidden) + size_t(r0) * D * xs;
       g.ldo = D;
       g.acc = nullptr;
@@ -157,8 +210,8 @@ flp_status flp_backward(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
       if (launch_dx(x_dtype, g, s) != hipSuccess) return FLP_HIP_ERROR;
     }
     if (d_weight) {
-      if (launch_transpose(x_dtype, h_chunk, rows, round_up(rows, 64), D, D, hT, L.ldt, s) !=
-          hipSuccess)
+      const int64_t kpad = round_up(rows, kTokPad);  // dz^T and hidden^T are zero past rows
+      if (launch_transpose(x_dtype, h_chunk, rows, kpad, D, D, hT, L.ldt, s) != hipSuccess)
         return FLP_HIP_ERROR;
       GemmArgs g;
       g.a = dzT;
@@ -167,7 +220,7 @@ flp_status flp_backward(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
       g.ldb_b = L.ldt * int64_t(xs);
       g.M = V;
       g.N = D;
-      g.K = rows;
+      g.K = kpad;
       g.out = d_weight;
       g.ldo = D;
       g.acc = acc;
@@ -182,6 +235,31 @@ flp_status flp_backward(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
     }
   }
   return FLP_OK;
+}
+
+void flp_profile_enable(int on) { g_prof_on.store(on != 0); }
+
+flp_status flp_profile_read(double* ms, int64_t* count, int n) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  const int m = n < FLP_K_COUNT ? n : FLP_K_COUNT;
+  for (int k = 0; k < m; ++k) {
+    ms[k] = 0.0;
+    count[k] = 0;
+  }
+  flp_status st = FLP_OK;
+  for (const ProfRec& r : g_prof_recs) {
+    float t = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&t, r.a, r.b) != hipSuccess)
+      st = FLP_HIP_ERROR;
+    else if (r.kind < m) {
+      ms[r.kind] += double(t);
+      count[r.kind] += 1;
+    }
+    g_prof_pool.push_back(r.a);
+    g_prof_pool.push_back(r.b);
+  }
+  g_prof_recs.clear();
+  return st;
 }
 
 const char* flp_status_string(flp_status status) {

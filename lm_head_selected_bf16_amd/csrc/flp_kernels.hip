@@ -2,30 +2,38 @@
 //
 // Forward ("Fused Linear LogP" docs page, sections "Backends" and "Reference
 // Semantics"): each workgroup computes one [BM x 256] tile of scaled logits
-// z = (h W^T + b) / T with bf16 (or fp32) MFMA and fp32 accumulation, then
-// folds the tile into a per-row (max, sum of exp) pair and picks up the target
-// logit; a merge kernel folds the pairs of all vocabulary tiles in ascending
-// order into lse and logp.  The [N, V] logits never reach HBM.
+// z = (h W^T + b) / T with bf16 (or fp32) MFMA and fp32 accumulation, folds
+// the tile into a per-row (max, sum of exp) pair and picks up the target
+// logit; a merge kernel folds the pairs of all vocabulary tiles into lse and
+// logp.  The [N, V] logits never reach HBM.
 //
 // Backward (PR #234, "Implementation details"; PR #555 summary): per row
 // chunk, a dlogits kernel recomputes the same logit tiles and writes
-// dz = G (onehot - exp(z - lse)) / T; two MFMA GEMMs give d_hidden = dz W and
-// d_weight += dz^T hidden with a fixed ascending K order; d_bias partials are
-// folded in ascending row-tile order.  No atomics anywhere.
+// dz = G (onehot - exp(z - lse)) / T row-major and transposed; two GEMMs give
+// d_hidden = dz W and d_weight (+)= dz^T hidden, each with one fixed ascending
+// K order; d_bias partials are folded in ascending row-tile order.  No atomics.
 //
-// Register layout.  Every MFMA is issued as mfma(A = N-side fragment,
-// B = M-side fragment), so lane l of a wave holds output row (l % 16) of a
-// 16-row block and four consecutive output columns 4*(l / 16) + 0..3 of a
-// 16-column block.  Both operand fragments are 16 bytes of K read from LDS at
-// (row l % 16, 16-byte chunk l / 16).
+// One MFMA engine serves all four contractions.  Every operand is stored
+// K-contiguous (W is transposed once per backward for d_hidden; hidden per
+// chunk for d_weight) and streamed by direct global->LDS loads
+// (global_load_lds_dwordx4, no register staging) into two LDS stages of
+// 128 bytes of K per row.  Waves form a WM x WN grid; each wave owns a
+// (BM/WM) x (BN/WN) block of 16 x 16 MFMA tiles with its fp32 accumulators in
+// AGPRs, and double-buffers its operand fragments across the two 64-byte
+// halves of a stage.
 //
-// Batch invariance.  For every logit the MFMA chain over K is the same
-// (ascending 128-byte stages, same instruction, same lane placement of K), and
-// the per-row reductions over a 256-column vocabulary tile use one fixed tree
-// defined by column positions only: within a lane over its 4 columns and 4
-// column blocks, across the four 16-lane groups by xor-butterfly, then across
-// the four 64-column waves in ascending order.  No kernel's per-row arithmetic
-// depends on N, the row tile size or the row's position.
+// Register layout: every MFMA is issued as mfma(A = N-side fragment,
+// B = M-side fragment), so lane l holds output row (l % 16) of a 16-row block
+// and four consecutive output columns 4 (l / 16) + 0..3 of a 16-column block.
+// Both fragments are 16 bytes of K read from LDS at (row l % 16, chunk l / 16).
+//
+// Batch invariance: every logit has the same MFMA chain over K (ascending
+// 64-byte steps, same instruction, same lane placement of K) and every
+// per-row reduction over a 256-column vocabulary tile uses one fixed tree
+// defined by column positions only: in-lane over the 4 columns x 8 column
+// blocks a lane holds of each 128-column half, across the four 16-lane groups
+// by xor-butterfly (16, then 32), then half 0 + half 1.  No per-row arithmetic
+// depends on N, the row tile or the row's position.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -41,9 +49,11 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kStageBytes = 128;  // bytes of K per operand row per pipeline stage
+constexpr int kStageBytes = 64;   // bytes of K per operand row per pipeline stage
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr int kGroupM = 8;        // row tiles per scheduling group
+constexpr int kTileCols = 256;    // vocabulary tile of the logits kernels
+constexpr int kHalfCols = 128;    // columns per wave column in the logits kernels
 
 struct BF16 {
   static constexpr int kSize = 2;
@@ -52,10 +62,11 @@ struct F32 {
   static constexpr int kSize = 4;
 };
 
-// LDS tiles hold rows of 8 16-byte chunks (one 128-byte stage of K).  Chunk c
-// of row r lives at chunk position c ^ f(r) to spread MFMA fragment reads and
-// transposed writes over the banks.
-__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r ^ (r >> 3)) & 7); }
+// LDS tiles hold rows of 4 16-byte chunks (one 64-byte stage of K).  Chunk c
+// of row r lives at chunk position c ^ ((r >> 2) & 3).  (A wave64 ds_read_b128
+// costs the same for every 16-byte-aligned pattern measured on gfx950; the
+// swizzle only keeps each 16-row fragment read spread over all positions.)
+__device__ __forceinline__ int swzf(int r) { return (r >> 2) & 3; }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -124,259 +135,226 @@ __device__ __forceinline__ void tile_of(int bid, int nbm, int nbn, int& tm, int&
   tn = in / gm;
 }
 
-// ---- global -> LDS staging ------------------------------------------------------------
-
-// Operand stored K-contiguous: row r at base + r * ld, K bytes [kb0, kb0 + 128).
-template <int ROWS, int NT>
-struct LoadK {
-  static constexpr int kChunks = ROWS * 8;
-  static constexpr int kPer = (kChunks + NT - 1) / NT;
-  u32x4 v[kPer];
-
-  __device__ __forceinline__ void load(const void* base, int64_t ld, int64_t row0, int64_t nrows,
-                                       int64_t kb0, int64_t kbytes, int tid) {
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int idx = tid + j * NT;
-      const int r = idx >> 3, c = idx & 7;
-      const int64_t row = row0 + r;
-      const int64_t kb = kb0 + c * 16;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if ((kChunks % NT == 0 || idx < kChunks) && row < nrows && kb < kbytes)
-        x = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(base) + row * ld + kb);
-      v[j] = x;
-    }
-  }
-  __device__ __forceinline__ void store(u32x4* lds, int tid) const {
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int idx = tid + j * NT;
-      if (kChunks % NT == 0 || idx < kChunks) {
-        const int r = idx >> 3, c = idx & 7;
-        lds[r * 8 + swz(r, c)] = v[j];
-      }
-    }
-  }
-};
-
-// Operand stored M-contiguous ([K][M] in memory): each thread reads an 8 x 8
-// (bf16) or 4 x 4 (fp32) block of K rows x M columns and transposes it in
-// registers so that LDS holds M rows of contiguous K, as for LoadK.
-template <class E, int ROWS, int NT>
-struct LoadT;
-
-template <int ROWS, int NT>
-struct LoadT<BF16, ROWS, NT> {
-  static constexpr int kMC = ROWS / 8;            // 8-column chunks of M
-  static constexpr int kBlocks = kMC * 8;         // x 8 groups of 8 K rows (64 K per stage)
-  static constexpr int kPer = (kBlocks + NT - 1) / NT;
-  u32x4 v[kPer][8];
-
-  __device__ __forceinline__ void load(const void* base, int64_t ld, int64_t m0, int64_t mvalid,
-                                       int64_t k0, int64_t kvalid, int tid) {
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int idx = tid + j * NT;
-      const int mc = idx % kMC, kg = idx / kMC;
-      const int64_t m = m0 + mc * 8;
-      const bool live = (kBlocks % NT == 0 || idx < kBlocks) && m < mvalid;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int64_t k = k0 + kg * 8 + q;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (live && k < kvalid)
-          x = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(base) + k * ld + m * 2);
-        v[j][q] = x;
-      }
-    }
-  }
-  __device__ __forceinline__ void store(u32x4* lds, int tid) const {
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int idx = tid + j * NT;
-      if (kBlocks % NT == 0 || idx < kBlocks) {
-        const int mc = idx % kMC, kg = idx / kMC;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const int d = q >> 1;
-          const uint32_t sel = (q & 1) ? 0x07060302u : 0x05040100u;
-          u32x4 o;
-          o.x = __builtin_amdgcn_perm(v[j][1][d], v[j][0][d], sel);
-          o.y = __builtin_amdgcn_perm(v[j][3][d], v[j][2][d], sel);
-          o.z = __builtin_amdgcn_perm(v[j][5][d], v[j][4][d], sel);
-          o.w = __builtin_amdgcn_perm(v[j][7][d], v[j][6][d], sel);
-          const int r = mc * 8 + q;
-          lds[r * 8 + swz(r, kg)] = o;
-        }
-      }
-    }
-  }
-};
-
-template <int ROWS, int NT>
-struct LoadT<F32, ROWS, NT> {
-  static constexpr int kMC = ROWS / 4;            // 4-column chunks of M
-  static constexpr int kBlocks = kMC * 8;         // x 8 groups of 4 K rows (32 K per stage)
-  static constexpr int kPer = (kBlocks + NT - 1) / NT;
-  u32x4 v[kPer][4];
-
-  __device__ __forceinline__ void load(const void* base, int64_t ld, int64_t m0, int64_t mvalid,
-                                       int64_t k0, int64_t kvalid, int tid) {
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int idx = tid + j * NT;
-      const int mc = idx % kMC, kg = idx / kMC;
-      const int64_t m = m0 + mc * 4;
-      const bool live = (kBlocks % NT == 0 || idx < kBlocks) && m < mvalid;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t k = k0 + kg * 4 + q;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (live && k < kvalid)
-          x = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(base) + k * ld + m * 4);
-        v[j][q] = x;
-      }
-    }
-  }
-  __device__ __forceinline__ void store(u32x4* lds, int tid) const {
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int idx = tid + j * NT;
-      if (kBlocks % NT == 0 || idx < kBlocks) {
-        const int mc = idx % kMC, kg = idx / kMC;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          u32x4 o;
-          o.x = v[j][0][q];
-          o.y = v[j][1][q];
-          o.z = v[j][2][q];
-          o.w = v[j][3][q];
-          const int r = mc * 4 + q;
-          lds[r * 8 + swz(r, kg)] = o;
-        }
-      }
-    }
-  }
-};
-
-// ---- the MFMA K loop ----------------------------------------------------------------------
-
-template <class E, int WMB, int WNB>
-__device__ __forceinline__ void compute_stage(f32x4_t (&acc)[WMB][WNB], const u32x4* As,
-                                              const u32x4* Bs, int arow0, int brow0, int i, int g) {
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    u32x4 af[WMB], bf[WNB];
-#pragma unroll
-    for (int mb = 0; mb < WMB; ++mb) {
-      const int r = arow0 + mb * 16 + i;
-      af[mb] = As[r * 8 + swz(r, h * 4 + g)];
-    }
-#pragma unroll
-    for (int nb = 0; nb < WNB; ++nb) {
-      const int r = brow0 + nb * 16 + i;
-      bf[nb] = Bs[r * 8 + swz(r, h * 4 + g)];
-    }
-#pragma unroll
-    for (int mb = 0; mb < WMB; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < WNB; ++nb) mma64<E>(acc[mb][nb], bf[nb], af[mb]);
-  }
-}
-
-// Two LDS buffers per operand; global loads for stage s+1 are in flight in
-// registers while stage s is multiplied.  One barrier per stage.
-template <class E, int WMB, int WNB, class LoadFn, class StoreFn>
-__device__ __forceinline__ void kloop(f32x4_t (&acc)[WMB][WNB], int nst, u32x4* sA0, u32x4* sA1,
-                                      u32x4* sB0, u32x4* sB1, int arow0, int brow0, int lane,
-                                      LoadFn&& load, StoreFn&& store) {
-  const int i = lane & 15, g = lane >> 4;
-  load(0);
-  store(sA0, sB0);
-  __syncthreads();
-  for (int st = 0; st < nst; ++st) {
-    const bool more = st + 1 < nst;
-    if (more) load(st + 1);
-    const bool odd = st & 1;
-    compute_stage<E, WMB, WNB>(acc, odd ? sA1 : sA0, odd ? sB1 : sB0, arow0, brow0, i, g);
-    if (more) store(odd ? sA0 : sA1, odd ? sB0 : sB1);
-    __syncthreads();
-  }
-}
-
-// ---- logits tile shared by the forward and dlogits kernels ---------------------------------
+// ---- direct global -> LDS staging of one operand tile --------------------------------------
 //
-// Workgroup = WAVES_M x 4 waves; wave (wm, wn) owns rows [wm*RW, wm*RW + RW) and the
-// 64 vocabulary columns [wn*64, wn*64 + 64) of the BM x 256 tile.
-template <class E, int BM, int WAVES_M>
-struct LogitTile {
-  static constexpr int NT = 256 * WAVES_M;
-  static constexpr int BN = 256;
-  static constexpr int RW = BM / WAVES_M;
-  static constexpr int WMB = RW / 16;
-  static constexpr int WNB = 4;
-  static constexpr size_t kLds = size_t(2) * (BM + BN) * kStageBytes;
-  static_assert(RW % 16 == 0, "rows per wave must be a multiple of 16");
+// ROWS rows x 64 bytes per stage.  One wave instruction fills 64 consecutive
+// 16-byte LDS slots (lane i -> slot base + i): instruction inst covers rows
+// 16*inst + lane / 4, chunk position lane % 4, i.e. logical chunk
+// (lane % 4) ^ ((lane >> 4) & 3).  Rows past the end of the operand read a
+// clamped (valid) row whose results are never used.
+template <int ROWS, int NW>
+struct DTile {
+  static constexpr int kInsts = ROWS / 16;
+  static constexpr int kPer = (kInsts + NW - 1) / NW;
+  // Wave w issues instructions w*kPer .. min(kInsts, (w+1)*kPer) - 1, so the last
+  // waves may issue fewer; kMin is the fewest any wave issues per stage.
+  static constexpr int kMin = kInsts - (NW - 1) * kPer > 0 ? kInsts - (NW - 1) * kPer : 0;
+  static_assert(ROWS % 16 == 0, "tile rows must be a multiple of 16");
+  uint32_t q, voff;     // q = lane / 4; voff = q * ld + chunk * 16
+  uint32_t coff;
+  int64_t ld, rows_valid;
+  bool full;            // every row of the tile is valid: no clamping
 
-  __device__ __forceinline__ static void run(f32x4_t (&acc)[WMB][WNB], const void* hidden,
-                                             const void* weight, int64_t row0, int64_t nrows,
-                                             int64_t col0, int64_t V, int64_t D, u32x4* smem) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wn = wave & 3, wm = wave >> 2;
-    const int64_t kbytes = D * E::kSize;
-    const int nst = int((kbytes + kStageBytes - 1) / kStageBytes);
-    u32x4* sA0 = smem;
-    u32x4* sA1 = smem + BM * 8;
-    u32x4* sB0 = smem + 2 * BM * 8;
-    u32x4* sB1 = sB0 + BN * 8;
+  __device__ __forceinline__ void init(int64_t ld_, int64_t rows_valid_, int lane) {
+    ld = ld_;
+    rows_valid = rows_valid_;
+    full = rows_valid_ >= ROWS;
+    q = uint32_t(lane >> 2);
+    coff = uint32_t(((lane & 3) ^ ((lane >> 4) & 3)) * 16);
+    voff = uint32_t(int64_t(q) * ld_) + coff;
+  }
+  __device__ __forceinline__ void issue(const char* base, uint32_t kb0, u32x4* lds, int wave) const {
+    const char* sb = base + kb0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int inst = wave * kPer + j;
+      if (kInsts % NW == 0 || inst < kInsts) {
+        uint32_t off;
+        if (full) {
+          off = uint32_t(inst * 16) * uint32_t(ld) + voff;
+        } else {
+          int64_t r = int64_t(inst) * 16 + q;
+          r = r < rows_valid ? r : rows_valid - 1;
+          off = uint32_t(r * ld) + coff;
+        }
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(sb + off),
+                                         (__attribute__((address_space(3))) void*)(lds + inst * 64),
+                                         16, 0, 0);
+      }
+    }
+  }
+};
+
+// Wait until at most N of this wave's vector-memory loads are outstanding, then
+// barrier the workgroup.  The direct loads complete in issue order.
+template <int N>
+__device__ __forceinline__ void wait_loads_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// ---- the MFMA engine -------------------------------------------------------------------------
+//
+// A ring of NS LDS stages; stage s of K lives in buffer s % NS.  Loads of stage
+// s + NS - 1 are issued while stage s is multiplied, and the fragments of stage
+// s + 1 are read from LDS in between the MFMAs of stage s.
+template <class E, int BM, int BN, int WM, int WN, int NS>
+struct Engine {
+  static constexpr int NW = WM * WN;
+  static constexpr int NT = 64 * NW;
+  static constexpr int RW = BM / WM;
+  static constexpr int CW = BN / WN;
+  static constexpr int WMB = RW / 16;
+  static constexpr int WNB = CW / 16;
+  static constexpr int kSlots = (BM + BN) * 4;  // 16-byte LDS slots per stage
+  static constexpr size_t kStage = size_t(kSlots) * 16;
+  static constexpr size_t kLds = NS * kStage;
+  // Loads per stage of the wave that issues the fewest.  Waiting until at most
+  // k * kLoads loads are outstanding therefore guarantees, for every wave, that
+  // all but its last k stages have landed (waves with more loads wait a little
+  // longer than needed).
+  static constexpr int kLoads = DTile<BM, NW>::kMin + DTile<BN, NW>::kMin;
+  static_assert(RW % 16 == 0 && CW % 16 == 0, "wave tile must be a multiple of 16");
+  static_assert(NS >= 3, "the ring needs at least three stages");
+
+  struct Frag {
+    u32x4 a[WMB], b[WNB];
+  };
+
+  // Fragments of the stage at slot offset `st`: per-lane base slots fa, fb; the
+  // 16-row blocks are immediate offsets (64 slots apart).
+  __device__ __forceinline__ static void read(Frag& f, const u32x4* st, int fa, int fb) {
+#pragma unroll
+    for (int mb = 0; mb < WMB; ++mb) f.a[mb] = st[fa + mb * 64];
+#pragma unroll
+    for (int nb = 0; nb < WNB; ++nb) f.b[nb] = st[BM * 4 + fb + nb * 64];
+  }
+
+  __device__ __forceinline__ static void mmas(f32x4_t (&acc)[WMB][WNB], const Frag& f) {
 #pragma unroll
     for (int mb = 0; mb < WMB; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < WNB; ++nb) acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    LoadK<BM, NT> la;
-    LoadK<BN, NT> lb;
-    kloop<E, WMB, WNB>(
-        acc, nst, sA0, sA1, sB0, sB1, wm * RW, wn * 64, lane,
-        [&](int st) {
-          la.load(hidden, kbytes, row0, nrows, int64_t(st) * kStageBytes, kbytes, tid);
-          lb.load(weight, kbytes, col0, V, int64_t(st) * kStageBytes, kbytes, tid);
-        },
-        [&](u32x4* a, u32x4* b) {
-          la.store(a, tid);
-          lb.store(b, tid);
-        });
+      for (int nb = 0; nb < WNB; ++nb) mma64<E>(acc[mb][nb], f.b[nb], f.a[mb]);
+  }
+
+  // acc (+)= A[rows, K] . B[rows, K]^T over kbytes of K (a multiple of 64; ODD when
+  // kbytes / 64 is odd).  a and b point at the first row of the tile; rows past
+  // *_rows_valid are clamped.
+  template <bool ODD>
+  __device__ __forceinline__ static void run(f32x4_t (&acc)[WMB][WNB], const char* a, int64_t lda,
+                                             int64_t a_rows_valid, const char* b, int64_t ldb,
+                                             int64_t b_rows_valid, int64_t kbytes, u32x4* smem) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave % WM, wn = wave / WM, i = lane & 15, g = lane >> 4;
+    const int nst = int(kbytes / kStageBytes);
+    DTile<BM, NW> ta;
+    DTile<BN, NW> tb;
+    ta.init(lda, a_rows_valid, lane);
+    tb.init(ldb, b_rows_valid, lane);
+    const int pos = g ^ swzf(i);
+    const int fa = (wm * RW + i) * 4 + pos;
+    const int fb = (wn * CW + i) * 4 + pos;
+    auto issue = [&](int st) {
+      u32x4* dst = smem + (st % NS) * kSlots;
+      ta.issue(a, uint32_t(st) * kStageBytes, dst, wave);
+      tb.issue(b, uint32_t(st) * kStageBytes, dst + BM * 4, wave);
+    };
+#pragma unroll
+    for (int st = 0; st < NS - 1; ++st)
+      if (st < nst) issue(st);
+    if (nst > NS - 2)
+      wait_loads_barrier<kLoads * (NS - 2)>();
+    else
+      wait_loads_barrier<0>();
+    // One step: wait for stage st + 1, refill the ring, read st + 1 into `nxt` while
+    // multiplying stage st from `cur`.  The last step re-reads the last stage
+    // (unused) so that every step has the same straight-line body.
+    auto step = [&](int st, const Frag& cur, Frag& nxt) {
+      if (st + NS - 1 < nst)
+        wait_loads_barrier<kLoads * (NS - 3)>();
+      else
+        wait_loads_barrier<0>();
+      if (st + NS - 1 < nst) issue(st + NS - 1);  // into the buffer of stage st - 1
+      const int rd = st + 1 < nst ? st + 1 : st;
+      read(nxt, smem + (rd % NS) * kSlots, fa, fb);
+      mmas(acc, cur);
+      // Keep the reads of stage st + 1 spread among the MFMAs of stage st.
+      constexpr int kR = WMB + WNB, kM = WMB * WNB * (E::kSize == 2 ? 1 : 4);
+      constexpr int kStep = kM / kR > 0 ? kM / kR : 1;
+#pragma unroll
+      for (int k = 0; k < kR; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, kStep, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kM - kStep * kR, 0);
+    };
+    Frag f0, f1;
+    read(f0, smem, fa, fb);
+    if constexpr (!ODD) {
+      for (int st = 0; st < nst; st += 2) {
+        step(st, f0, f1);
+        step(st + 1, f1, f0);
+      }
+    } else {
+      step(0, f0, f1);
+      for (int st = 1; st < nst; st += 2) {
+        step(st, f1, f0);
+        step(st + 1, f0, f1);
+      }
+    }
   }
 };
 
 // ---- forward: logits tile -> per-row (max, sum of exp) partial + target logit -------------
-template <class E, int BM, int WAVES_M>
-__global__ __launch_bounds__(256 * WAVES_M) void k_fwd(FwdArgs p) {
-  using Tile = LogitTile<E, BM, WAVES_M>;
-  constexpr int RW = Tile::RW, WMB = Tile::WMB, WNB = Tile::WNB, NT = Tile::NT;
+//
+// Workgroup = WM x 2 waves; wave (wm, wn) owns rows [wm*RW, wm*RW + RW) and the 128
+// vocabulary columns [wn*128, wn*128 + 128) of the BM x 256 tile.
+template <class E, int BM, int WM>
+using LogitEngine = Engine<E, BM, kTileCols, WM, 2, (BM <= 32 ? 4 : 5)>;
+
+// The fixed per-row tree over the 32 values one lane holds of a wave's 128 columns.
+template <int WNB>
+__device__ __forceinline__ float lane_sum(const float (&e)[WNB][4]) {
+  static_assert(WNB == 8, "the reduction tree is defined for 8 column blocks per wave");
+  float s[WNB];
+#pragma unroll
+  for (int nb = 0; nb < WNB; ++nb) s[nb] = (e[nb][0] + e[nb][1]) + (e[nb][2] + e[nb][3]);
+  return ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
+}
+
+template <class E, int BM, int WM, bool ODD>
+__global__ __launch_bounds__(128 * WM) void k_fwd(FwdArgs p) {
+  using Eng = LogitEngine<E, BM, WM>;
+  constexpr int RW = Eng::RW, WMB = Eng::WMB, WNB = Eng::WNB, NT = Eng::NT;
   extern __shared__ u32x4 smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wn = wave & 3, wm = wave >> 2, i = lane & 15, g = lane >> 4;
+  const int wm = wave % WM, wn = wave / WM, i = lane & 15, g = lane >> 4;
   const int nbm = int((p.N + BM - 1) / BM);
-  const int nbn = int((p.V + 255) / 256);
+  const int nbn = int((p.V + kTileCols - 1) / kTileCols);
   int tm, tn;
   tile_of(blockIdx.x, nbm, nbn, tm, tn);
-  const int64_t row0 = int64_t(tm) * BM, col0 = int64_t(tn) * 256;
+  const int64_t row0 = int64_t(tm) * BM, col0 = int64_t(tn) * kTileCols;
+  const int64_t kbytes = p.D * E::kSize;
 
   f32x4_t acc[WMB][WNB];
-  Tile::run(acc, p.hidden, p.weight, row0, p.N, col0, p.V, p.D, smem);
+#pragma unroll
+  for (int mb = 0; mb < WMB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < WNB; ++nb) acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  Eng::template run<ODD>(acc, reinterpret_cast<const char*>(p.hidden) + row0 * kbytes, kbytes, p.N - row0,
+           reinterpret_cast<const char*>(p.weight) + col0 * kbytes, kbytes, p.V - col0, kbytes,
+           smem);
 
-  float* red = reinterpret_cast<float*>(smem);  // [4][BM] row max, then [4][BM] row sums
-  const int64_t cw = col0 + wn * 64;
+  float* red = reinterpret_cast<float*>(smem);  // [2][BM] row max, then [2][BM] row sums
+  const int64_t cw = col0 + wn * kHalfCols;
   float bcol[WNB][4];
-  bool cval[WNB][4];
 #pragma unroll
   for (int nb = 0; nb < WNB; ++nb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int64_t c = cw + nb * 16 + 4 * g + r;
-      cval[nb][r] = c < p.V;
       bcol[nb][r] = (p.bias != nullptr && c < p.V) ? p.bias[c] : 0.f;
     }
+  const int64_t vlim = p.V - cw;  // columns of this wave at or past vlim are padding
 
 #pragma unroll
   for (int mb = 0; mb < WMB; ++mb) {
@@ -389,7 +367,7 @@ __global__ __launch_bounds__(256 * WAVES_M) void k_fwd(FwdArgs p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float z = (acc[mb][nb][r] + bcol[nb][r]) * invT;
-        z = cval[nb][r] ? z : -INFINITY;
+        z = (nb * 16 + 4 * g + r < vlim) ? z : -INFINITY;
         acc[mb][nb][r] = z;
         mx = fmaxf(mx, z);
       }
@@ -402,24 +380,20 @@ __global__ __launch_bounds__(256 * WAVES_M) void k_fwd(FwdArgs p) {
   for (int mb = 0; mb < WMB; ++mb) {
     const int rl = wm * RW + mb * 16 + i;
     const int64_t row = row0 + rl;
-    const float M = fmaxf(fmaxf(red[rl], red[BM + rl]), fmaxf(red[2 * BM + rl], red[3 * BM + rl]));
-    float sb[WNB];
+    const float M = fmaxf(red[rl], red[BM + rl]);
+    float e[WNB][4];
 #pragma unroll
-    for (int nb = 0; nb < WNB; ++nb) {
-      const float e0 = fast_exp2((acc[mb][nb][0] - M) * kLog2e);
-      const float e1 = fast_exp2((acc[mb][nb][1] - M) * kLog2e);
-      const float e2 = fast_exp2((acc[mb][nb][2] - M) * kLog2e);
-      const float e3 = fast_exp2((acc[mb][nb][3] - M) * kLog2e);
-      sb[nb] = (e0 + e1) + (e2 + e3);
-    }
-    float s = (sb[0] + sb[1]) + (sb[2] + sb[3]);
+    for (int nb = 0; nb < WNB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) e[nb][r] = fast_exp2((acc[mb][nb][r] - M) * kLog2e);
+    float s = lane_sum<WNB>(e);
     s += __shfl_xor(s, 16);
     s += __shfl_xor(s, 32);
-    if (g == 0) red[4 * BM + wn * BM + rl] = s;
+    if (g == 0) red[2 * BM + wn * BM + rl] = s;
     if (row < p.N) {
       const int64_t t = load_target(p.targets, p.t64, row);
       const int64_t rel = t - cw;
-      if (t >= 0 && t < p.V && rel >= 0 && rel < 64 && int((rel & 15) >> 2) == g) {
+      if (t >= 0 && t < p.V && rel >= 0 && rel < kHalfCols && int((rel & 15) >> 2) == g) {
         const int tnb = int(rel >> 4), tr = int(rel & 3);
         float zt = 0.f;
 #pragma unroll
@@ -434,9 +408,8 @@ __global__ __launch_bounds__(256 * WAVES_M) void k_fwd(FwdArgs p) {
   for (int rl = tid; rl < BM; rl += NT) {
     const int64_t row = row0 + rl;
     if (row < p.N) {
-      const float M = fmaxf(fmaxf(red[rl], red[BM + rl]), fmaxf(red[2 * BM + rl], red[3 * BM + rl]));
-      const float* sr = red + 4 * BM;
-      const float S = ((sr[rl] + sr[BM + rl]) + sr[2 * BM + rl]) + sr[3 * BM + rl];
+      const float M = fmaxf(red[rl], red[BM + rl]);
+      const float S = red[2 * BM + rl] + red[3 * BM + rl];
       p.part[int64_t(tn) * p.N + row] = make_float2(M, S);
     }
   }
@@ -444,8 +417,8 @@ __global__ __launch_bounds__(256 * WAVES_M) void k_fwd(FwdArgs p) {
 
 // ---- merge: ascending fold of the per-tile pairs -> lse, logp --------------------------------
 //
-// 256 threads = 32 rows x 8 segments of vocabulary tiles.  Each thread folds its
-// segment in ascending order, then one thread per row folds the 8 segment
+// 256 threads = 8 rows x 32 segments of vocabulary tiles.  Each thread folds its
+// segment in ascending order, then one thread per row folds the 32 segment
 // results in ascending order.  The topology depends on V only.
 __device__ __forceinline__ void fold(float& M, float& S, float m, float s) {
   if (m == -INFINITY) return;
@@ -456,17 +429,23 @@ __device__ __forceinline__ void fold(float& M, float& S, float m, float s) {
   M = Mn;
 }
 
+constexpr int kMergeRows = 8, kMergeSegs = 32;
+
 __global__ __launch_bounds__(256) void k_merge(MergeArgs p) {
-  __shared__ float sm[8][32], ss[8][32];
-  const int rl = threadIdx.x & 31, seg = threadIdx.x >> 5;
-  const int64_t row = int64_t(blockIdx.x) * 32 + rl;
-  const int64_t seglen = (p.n_vt + 7) / 8;
+  __shared__ float sm[kMergeSegs][kMergeRows], ss[kMergeSegs][kMergeRows];
+  const int rl = threadIdx.x % kMergeRows, seg = threadIdx.x / kMergeRows;
+  const int64_t row = int64_t(blockIdx.x) * kMergeRows + rl;
+  const int64_t seglen = (p.n_vt + kMergeSegs - 1) / kMergeSegs;
   float M = -INFINITY, S = 0.f;
   if (row < p.N) {
-    const int64_t v0 = seg * seglen, v1 = min(p.n_vt, v0 + seglen);
-    for (int64_t v = v0; v < v1; ++v) {
-      const float2 q = p.part[v * p.N + row];
-      fold(M, S, q.x, q.y);
+    const int64_t v1 = min(p.n_vt, (seg + 1) * seglen);
+    for (int64_t v0 = seg * seglen; v0 < v1; v0 += 8) {
+      float2 q[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        q[u] = (v0 + u < v1) ? p.part[(v0 + u) * p.N + row] : make_float2(-INFINITY, 0.f);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) fold(M, S, q[u].x, q[u].y);
     }
   }
   sm[seg][rl] = M;
@@ -475,7 +454,7 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs p) {
   if (seg == 0 && row < p.N) {
     float M2 = -INFINITY, S2 = 0.f;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) fold(M2, S2, sm[k][rl], ss[k][rl]);
+    for (int k = 0; k < kMergeSegs; ++k) fold(M2, S2, sm[k][rl], ss[k][rl]);
     const float ls = logf(S2);
     const int64_t t = load_target(p.targets, p.t64, row);
     const bool valid = t >= 0 && t < p.V;
@@ -487,39 +466,52 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs p) {
 // ---- dlogits: recompute the logit tile, dz = G (onehot - p) / T, d_bias partials ------------
 //
 // dz is written row-major ([token][vocab], for d_hidden = dz W) and transposed
-// ([vocab][token], for d_weight = dz^T hidden) so that both GEMMs read K-contiguous
-// operands.  The transposed copy goes through LDS in passes of CPP columns so
-// that every vocabulary row receives BM contiguous tokens.
-template <class E>
-__device__ __forceinline__ void lds_put(char* base, int idx, float v);
-template <>
-__device__ __forceinline__ void lds_put<BF16>(char* base, int idx, float v) {
-  reinterpret_cast<uint16_t*>(base)[idx] = uint16_t(bf16_bits_rne(v));
-}
-template <>
-__device__ __forceinline__ void lds_put<F32>(char* base, int idx, float v) {
-  reinterpret_cast<float*>(base)[idx] = v;
+// ([vocab][token], for d_weight = dz^T hidden) so that both GEMMs read
+// K-contiguous operands.  The transposed copy goes through LDS in passes of
+// CPP columns so that every vocabulary row receives BM contiguous tokens.
+// LDS staging of the transposed tile (bf16): [256 columns][BM tokens], each
+// column row padded by 16 bytes.
+template <int BM>
+struct DzT {
+  static constexpr int kRowB = BM * 2 + 16;
+  static constexpr size_t kBytes = size_t(kTileCols) * kRowB;
+};
+
+template <class E, int BM, int WM>
+constexpr size_t dz_lds() {
+  using Eng = LogitEngine<E, BM, WM>;
+  return (E::kSize == 2 && DzT<BM>::kBytes > Eng::kLds) ? DzT<BM>::kBytes : Eng::kLds;
 }
 
-template <class E, int BM, int WAVES_M>
-__global__ __launch_bounds__(256 * WAVES_M) void k_dz(DzArgs p) {
-  using Tile = LogitTile<E, BM, WAVES_M>;
-  constexpr int RW = Tile::RW, WMB = Tile::WMB, WNB = Tile::WNB, NT = Tile::NT;
+template <class E, int BM, int WM, bool ODD>
+__global__ __launch_bounds__(128 * WM) void k_dz(DzArgs p) {
+  using Eng = LogitEngine<E, BM, WM>;
+  constexpr int RW = Eng::RW, WMB = Eng::WMB, WNB = Eng::WNB, NT = Eng::NT;
+  constexpr bool kStageT = E::kSize == 2;  // bf16: transpose through LDS
   extern __shared__ u32x4 smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wn = wave & 3, wm = wave >> 2, i = lane & 15, g = lane >> 4;
+  const int wm = wave % WM, wn = wave / WM, i = lane & 15, g = lane >> 4;
   const int nbm = int((p.rows + BM - 1) / BM);
-  const int nbn = int((p.V + 255) / 256);
+  const int nbn = int((p.V + kTileCols - 1) / kTileCols);
   int tm, tn;
   tile_of(blockIdx.x, nbm, nbn, tm, tn);
-  const int64_t row0 = int64_t(tm) * BM, col0 = int64_t(tn) * 256;
+  const int64_t row0 = int64_t(tm) * BM, col0 = int64_t(tn) * kTileCols;
+  const int64_t kbytes = p.D * E::kSize;
 
   f32x4_t acc[WMB][WNB];
-  Tile::run(acc, p.hidden, p.weight, row0, p.rows, col0, p.V, p.D, smem);
+#pragma unroll
+  for (int mb = 0; mb < WMB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < WNB; ++nb) acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  Eng::template run<ODD>(acc, reinterpret_cast<const char*>(p.hidden) + row0 * kbytes, kbytes, p.rows - row0,
+           reinterpret_cast<const char*>(p.weight) + col0 * kbytes, kbytes, p.V - col0, kbytes,
+           smem);
+  __syncthreads();  // every wave is done with the operand stages: LDS is reused below
 
-  const int64_t cw = col0 + wn * 64;
+  const int64_t cw = col0 + wn * kHalfCols;
+  const int64_t vlim = p.V - cw;
+  char* lds = reinterpret_cast<char*>(smem);
   float bcol[WNB][4];
-  bool cval[WNB][4];
   f32x4_t csum[WNB];
 #pragma unroll
   for (int nb = 0; nb < WNB; ++nb) {
@@ -527,76 +519,66 @@ __global__ __launch_bounds__(256 * WAVES_M) void k_dz(DzArgs p) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int64_t c = cw + nb * 16 + 4 * g + r;
-      cval[nb][r] = c < p.V;
       bcol[nb][r] = (p.bias != nullptr && c < p.V) ? p.bias[c] : 0.f;
     }
   }
 #pragma unroll
   for (int mb = 0; mb < WMB; ++mb) {
-    const int64_t row = row0 + wm * RW + mb * 16 + i;
+    const int tl = wm * RW + mb * 16 + i;  // token within the tile
+    const int64_t row = row0 + tl;
     const bool rv = row < p.rows;
     const float invT = (p.temperature != nullptr && rv) ? 1.0f / p.temperature[row] : 1.0f;
     const int64_t t = rv ? load_target(p.targets, p.t64, row) : -1;
     const bool valid = t >= 0 && t < p.V;
     const float G = valid ? p.grad_out[row] * invT : 0.f;
     const float L = rv ? p.lse[row] : 0.f;
+    const int64_t trel = t - cw;
 #pragma unroll
     for (int nb = 0; nb < WNB; ++nb) {
       f32x4_t d;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t c = cw + nb * 16 + 4 * g + r;
+        const int cl = nb * 16 + 4 * g + r;
         const float z = (acc[mb][nb][r] + bcol[nb][r]) * invT;
         const float pr = fast_exp2((z - L) * kLog2e);
-        const float oh = (c == t) ? 1.0f : 0.0f;
+        const float oh = (cl == trel) ? 1.0f : 0.0f;
         float v = G * (oh - pr);
-        v = (valid && cval[nb][r]) ? v : 0.0f;
+        v = (valid && cl < vlim) ? v : 0.0f;
         d[r] = v;
       }
-      acc[mb][nb] = d;
       csum[nb] += d;
       if (p.dz != nullptr) store4<E>(p.dz, row * p.ldz + cw + nb * 16 + 4 * g, d);
+      if (p.dzT != nullptr) {
+        const int cl = wn * kHalfCols + nb * 16 + 4 * g;  // column within the tile
+        if (kStageT) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            reinterpret_cast<uint16_t*>(lds + (cl + r) * DzT<BM>::kRowB)[tl] =
+                uint16_t(bf16_bits_rne(d[r]));
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            reinterpret_cast<float*>(p.dzT)[(col0 + cl + r) * p.ldt + row] = d[r];
+        }
+      }
     }
   }
-
-  char* lds = reinterpret_cast<char*>(smem);
-  if (p.dzT != nullptr) {
-    // LDS tile [CPP columns][BM tokens], each column row padded by 16 bytes.
-    constexpr int CPP = E::kSize == 2 ? 256 : 128;
-    constexpr int kRowB = BM * E::kSize + 16;
-    constexpr int kPitch = kRowB / E::kSize;
-    constexpr int kChunksPerCol = BM * E::kSize / 16;
-    constexpr int kTokPerChunk = 16 / E::kSize;
-    for (int pass = 0; pass < 256 / CPP; ++pass) {
-      __syncthreads();
-      if (wn * 64 >= pass * CPP && wn * 64 < (pass + 1) * CPP) {
-#pragma unroll
-        for (int mb = 0; mb < WMB; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < WNB; ++nb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int c = wn * 64 + nb * 16 + 4 * g + r - pass * CPP;
-              const int tok = wm * RW + mb * 16 + i;
-              lds_put<E>(lds, c * kPitch + tok, acc[mb][nb][r]);
-            }
-      }
-      __syncthreads();
-      for (int idx = tid; idx < CPP * kChunksPerCol; idx += NT) {
-        const int c = idx / kChunksPerCol, ch = idx % kChunksPerCol;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(lds + c * kRowB + ch * 16);
-        const int64_t vcol = col0 + pass * CPP + c;
-        const int64_t tok = row0 + ch * kTokPerChunk;
-        *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(p.dzT) +
-                                  (vcol * p.ldt + tok) * E::kSize) = v;
-      }
+  if (kStageT && p.dzT != nullptr) {
+    // Every vocabulary row of dz^T receives the tile's BM contiguous tokens.
+    constexpr int kChunksPerCol = BM * 2 / 16;
+    __syncthreads();
+    for (int idx = tid; idx < kTileCols * kChunksPerCol; idx += NT) {
+      const int c = idx / kChunksPerCol, ch = idx % kChunksPerCol;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(lds + c * DzT<BM>::kRowB + ch * 16);
+      *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.dzT) + (col0 + c) * p.ldt + row0 +
+                                ch * 8) = v;
     }
   }
   if (p.dbias_part == nullptr) return;
   // Column sums over the tile's rows: in-lane over row blocks, then a butterfly
   // over the 16 lanes holding the other rows, then ascending over row waves.
   __syncthreads();
-  float* red = reinterpret_cast<float*>(smem);  // [WAVES_M][256]
+  float* red = reinterpret_cast<float*>(smem);  // [WM][256]
 #pragma unroll
   for (int nb = 0; nb < WNB; ++nb)
 #pragma unroll
@@ -606,20 +588,70 @@ __global__ __launch_bounds__(256 * WAVES_M) void k_dz(DzArgs p) {
       x += __shfl_xor(x, 2);
       x += __shfl_xor(x, 4);
       x += __shfl_xor(x, 8);
-      if (i == 0) red[wm * 256 + wn * 64 + nb * 16 + 4 * g + r] = x;
+      if (i == 0) red[wm * kTileCols + wn * kHalfCols + nb * 16 + 4 * g + r] = x;
     }
   __syncthreads();
-  for (int c = tid; c < 256; c += NT) {
+  for (int c = tid; c < kTileCols; c += NT) {
     float s = red[c];
 #pragma unroll
-    for (int w = 1; w < WAVES_M; ++w) s += red[w * 256 + c];
+    for (int w = 1; w < WM; ++w) s += red[w * kTileCols + c];
     p.dbias_part[int64_t(tm) * p.ldz + col0 + c] = s;
   }
 }
 
-// ---- tiled transpose (hidden chunk -> hidden^T for the d_weight GEMM) -------------------------
-// dst[c][r] = src[r][c]; tokens r in [rows, rows_pad) are written as zeros so that
-// 16-byte loads straddling the end of the chunk read zeros.
+// ---- GEMMs of the backward ----------------------------------------------------------------
+//
+// C[M x N] (+)= sum_k A[m][k] B[n][k], both operands K-contiguous.
+//   d_hidden: M = tokens, N = D, K = V (padded); A = dz [tok][ldz], B = W^T [D][ldz].
+//   d_weight: M = V, N = D, K = tokens (padded); A = dz^T [V][ldt], B = hidden^T [D][ldt].
+// LOAD: start from the fp32 accumulator p.acc; STORE: 0 = element type to p.out,
+// 1 = fp32 to p.acc.
+template <class E, int BM, int BN, int WM, int WN, bool LOAD, int STORE>
+__global__ __launch_bounds__(64 * WM * WN) void k_gemm(GemmArgs p) {
+  using Eng = Engine<E, BM, BN, WM, WN, 5>;
+  constexpr int RW = Eng::RW, CW = Eng::CW, WMB = Eng::WMB, WNB = Eng::WNB;
+  extern __shared__ u32x4 smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % WM, wn = wave / WM, i = lane & 15, g = lane >> 4;
+  const int nbm = int((p.M + BM - 1) / BM), nbn = int((p.N + BN - 1) / BN);
+  int tm, tn;
+  tile_of(blockIdx.x, nbm, nbn, tm, tn);
+  const int64_t m0 = int64_t(tm) * BM, n0 = int64_t(tn) * BN;
+  const int64_t nl = n0 + wn * CW + 4 * g;
+
+  f32x4_t acc[WMB][WNB];
+#pragma unroll
+  for (int mb = 0; mb < WMB; ++mb) {
+    const int64_t m = m0 + wm * RW + mb * 16 + i;
+#pragma unroll
+    for (int nb = 0; nb < WNB; ++nb) {
+      f32x4_t x = {0.f, 0.f, 0.f, 0.f};
+      if (LOAD && m < p.M && nl + nb * 16 < p.N)
+        x = *reinterpret_cast<const f32x4_t*>(p.acc + m * p.N + nl + nb * 16);
+      acc[mb][nb] = x;
+    }
+  }
+  Eng::template run<false>(acc, reinterpret_cast<const char*>(p.a) + m0 * p.lda_b, p.lda_b, p.M - m0,
+           reinterpret_cast<const char*>(p.b) + n0 * p.ldb_b, p.ldb_b, p.N - n0,
+           p.K * E::kSize, smem);
+
+#pragma unroll
+  for (int mb = 0; mb < WMB; ++mb) {
+    const int64_t m = m0 + wm * RW + mb * 16 + i;
+    if (m >= p.M) continue;
+#pragma unroll
+    for (int nb = 0; nb < WNB; ++nb) {
+      if (nl + nb * 16 >= p.N) continue;
+      if (STORE == 1)
+        *reinterpret_cast<f32x4_t*>(p.acc + m * p.N + nl + nb * 16) = acc[mb][nb];
+      else
+        store4<E>(p.out, m * p.ldo + nl + nb * 16, acc[mb][nb]);
+    }
+  }
+}
+
+// ---- tiled transpose ---------------------------------------------------------------------------
+// dst[c][r] = src[r][c]; entries r in [rows, rows_pad) are written as zeros.
 template <class T>
 __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ src, int64_t rows,
                                                    int64_t rows_pad, int64_t cols, int64_t ld_src,
@@ -635,98 +667,6 @@ __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ src, in
   for (int k = ty; k < 64; k += 4) {
     const int64_t c = c0 + k, r = r0 + tx;
     if (r < rows_pad && c < cols) dst[c * ld_dst + r] = tile[tx][k];
-  }
-}
-
-// ---- GEMMs of the backward ----------------------------------------------------------------
-//
-// C[M x N] (+)= sum_k A(m, k) B(n, k).  A is the M-side operand, B the N-side one;
-// AT / BT mark an operand stored [K][M] (M-contiguous) instead of [M][K].
-//   d_hidden: M = tokens, N = D, K = V; A = dz [tok][V], B = W [V][D] (BT).
-//   d_weight: M = V, N = D, K = tokens; A = dz^T [V][tok], B = hidden^T [D][tok].
-template <class E, int ROWS, int NT, bool T>
-struct Loader;
-template <class E, int ROWS, int NT>
-struct Loader<E, ROWS, NT, false> {
-  LoadK<ROWS, NT> l;
-  __device__ __forceinline__ void load(const void* base, int64_t ld, int64_t r0, int64_t rvalid,
-                                       int64_t st, int64_t K, int tid) {
-    l.load(base, ld, r0, rvalid, st * kStageBytes, K * E::kSize, tid);
-  }
-  __device__ __forceinline__ void store(u32x4* lds, int tid) const { l.store(lds, tid); }
-};
-template <class E, int ROWS, int NT>
-struct Loader<E, ROWS, NT, true> {
-  LoadT<E, ROWS, NT> l;
-  __device__ __forceinline__ void load(const void* base, int64_t ld, int64_t r0, int64_t rvalid,
-                                       int64_t st, int64_t K, int tid) {
-    l.load(base, ld, r0, rvalid, st * (kStageBytes / E::kSize), K, tid);
-  }
-  __device__ __forceinline__ void store(u32x4* lds, int tid) const { l.store(lds, tid); }
-};
-
-// LOAD: start from the fp32 accumulator p.acc; STORE: 0 = element type to p.out,
-// 1 = fp32 to p.acc.
-template <class E, int BM, int BN, int WAVES_M, int WAVES_N, bool AT, bool BT, bool LOAD, int STORE>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm(GemmArgs p) {
-  constexpr int NT = 64 * WAVES_M * WAVES_N;
-  constexpr int RW = BM / WAVES_M, CW = BN / WAVES_N;
-  constexpr int WMB = RW / 16, WNB = CW / 16;
-  static_assert(RW % 16 == 0 && CW % 16 == 0, "wave tile must be a multiple of 16");
-  extern __shared__ u32x4 smem[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave % WAVES_M, wn = wave / WAVES_M, i = lane & 15, g = lane >> 4;
-  const int nbm = int((p.M + BM - 1) / BM), nbn = int((p.N + BN - 1) / BN);
-  int tm, tn;
-  tile_of(blockIdx.x, nbm, nbn, tm, tn);
-  const int64_t m0 = int64_t(tm) * BM, n0 = int64_t(tn) * BN;
-
-  // Row pointers of this lane's output rows; columns are then immediate offsets.
-  const int64_t nl = n0 + wn * CW + 4 * g;
-  f32x4_t acc[WMB][WNB];
-#pragma unroll
-  for (int mb = 0; mb < WMB; ++mb) {
-    const int64_t m = m0 + wm * RW + mb * 16 + i;
-    const float* arow = p.acc + (m < p.M ? m : 0) * p.N + nl;
-#pragma unroll
-    for (int nb = 0; nb < WNB; ++nb) {
-      f32x4_t x = {0.f, 0.f, 0.f, 0.f};
-      if (LOAD && m < p.M && nl + nb * 16 < p.N) x = *reinterpret_cast<const f32x4_t*>(arow + nb * 16);
-      acc[mb][nb] = x;
-    }
-  }
-
-  const int64_t kst = kStageBytes / E::kSize;
-  const int nst = int((p.K + kst - 1) / kst);
-  u32x4* sA0 = smem;
-  u32x4* sA1 = smem + BM * 8;
-  u32x4* sB0 = smem + 2 * BM * 8;
-  u32x4* sB1 = sB0 + BN * 8;
-  Loader<E, BM, NT, AT> la;
-  Loader<E, BN, NT, BT> lb;
-  kloop<E, WMB, WNB>(
-      acc, nst, sA0, sA1, sB0, sB1, wm * RW, wn * CW, lane,
-      [&](int st) {
-        la.load(p.a, p.lda_b, m0, AT ? p.lda_b / E::kSize : p.M, st, p.K, tid);
-        lb.load(p.b, p.ldb_b, n0, p.N, st, p.K, tid);
-      },
-      [&](u32x4* a, u32x4* b) {
-        la.store(a, tid);
-        lb.store(b, tid);
-      });
-
-#pragma unroll
-  for (int mb = 0; mb < WMB; ++mb) {
-    const int64_t m = m0 + wm * RW + mb * 16 + i;
-    if (m >= p.M) continue;
-#pragma unroll
-    for (int nb = 0; nb < WNB; ++nb) {
-      if (nl + nb * 16 >= p.N) continue;
-      if (STORE == 1)
-        *reinterpret_cast<f32x4_t*>(p.acc + m * p.N + nl + nb * 16) = acc[mb][nb];
-      else
-        store4<E>(p.out, m * p.ldo + nl + nb * 16, acc[mb][nb]);
-    }
   }
 }
 
@@ -749,98 +689,127 @@ hipError_t prepare(K kernel, size_t lds) {
                              hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
 }
 
-template <class E, int BM, int WM>
+template <class E, int BM, int WM, bool ODD>
 hipError_t fwd_cfg(const FwdArgs& a, hipStream_t s) {
-  using Tile = LogitTile<E, BM, WM>;
-  static hipError_t once = prepare(k_fwd<E, BM, WM>, Tile::kLds);
+  using Eng = LogitEngine<E, BM, WM>;
+  static hipError_t once = prepare(k_fwd<E, BM, WM, ODD>, Eng::kLds);
   if (once != hipSuccess) return once;
-  const int64_t blocks = ((a.N + BM - 1) / BM) * ((a.V + 255) / 256);
-  hipLaunchKernelGGL((k_fwd<E, BM, WM>), dim3(unsigned(blocks)), dim3(Tile::NT), Tile::kLds, s, a);
+  const int64_t blocks = ((a.N + BM - 1) / BM) * ((a.V + kTileCols - 1) / kTileCols);
+  hipLaunchKernelGGL((k_fwd<E, BM, WM, ODD>), dim3(unsigned(blocks)), dim3(Eng::NT), Eng::kLds, s,
+                     a);
   return hipGetLastError();
+}
+
+// Number of 64-byte K stages of a logits tile is odd (D * element size / 64).
+template <class E>
+bool odd_stages(int64_t D) {
+  return ((D * E::kSize) / kStageBytes) % 2 == 1;
+}
+
+template <class E, bool ODD>
+hipError_t fwd_rows(const FwdArgs& a, hipStream_t s) {
+  if (a.N <= 32) return fwd_cfg<E, 32, 2, ODD>(a, s);
+  if (a.N <= 64) return fwd_cfg<E, 64, 2, ODD>(a, s);
+  return fwd_cfg<E, 128, 2, ODD>(a, s);
 }
 
 template <class E>
 hipError_t fwd_dispatch(const FwdArgs& a, hipStream_t s) {
-  if (a.N <= 32) return fwd_cfg<E, 32, 1>(a, s);
-  if (a.N <= 64) return fwd_cfg<E, 64, 1>(a, s);
-  if (a.N <= 128) return fwd_cfg<E, 128, 1>(a, s);
-  return fwd_cfg<E, 256, 2>(a, s);
+  return odd_stages<E>(a.D) ? fwd_rows<E, true>(a, s) : fwd_rows<E, false>(a, s);
 }
 
-template <class E>
-hipError_t dz_dispatch(const DzArgs& a, hipStream_t s) {
-  constexpr int BM = int(kDzRowTile), WM = 1;
-  using Tile = LogitTile<E, BM, WM>;
-  static hipError_t once = prepare(k_dz<E, BM, WM>, Tile::kLds);
+template <class E, int BM, int WM, bool ODD>
+hipError_t dz_cfg(const DzArgs& a, hipStream_t s) {
+  using Eng = LogitEngine<E, BM, WM>;
+  constexpr size_t lds = dz_lds<E, BM, WM>();
+  static hipError_t once = prepare(k_dz<E, BM, WM, ODD>, lds);
   if (once != hipSuccess) return once;
-  const int64_t blocks = ((a.rows + BM - 1) / BM) * ((a.V + 255) / 256);
-  hipLaunchKernelGGL((k_dz<E, BM, WM>), dim3(unsigned(blocks)), dim3(Tile::NT), Tile::kLds, s, a);
+  const int64_t blocks = ((a.rows + BM - 1) / BM) * ((a.V + kTileCols - 1) / kTileCols);
+  hipLaunchKernelGGL((k_dz<E, BM, WM, ODD>), dim3(unsigned(blocks)), dim3(Eng::NT), lds, s, a);
   return hipGetLastError();
 }
 
-template <class E, int BM, int BN, int WM, int WN, bool AT, bool BT, bool LOAD, int STORE>
+template <class E, int BM, int BN, int WM, int WN, bool LOAD, int STORE>
 hipError_t gemm_cfg(const GemmArgs& a, hipStream_t s) {
-  constexpr size_t lds = size_t(2) * (BM + BN) * kStageBytes;
-  static hipError_t once = prepare(k_gemm<E, BM, BN, WM, WN, AT, BT, LOAD, STORE>, lds);
+  using Eng = Engine<E, BM, BN, WM, WN, 5>;
+  static hipError_t once = prepare(k_gemm<E, BM, BN, WM, WN, LOAD, STORE>, Eng::kLds);
   if (once != hipSuccess) return once;
   const int64_t blocks = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  hipLaunchKernelGGL((k_gemm<E, BM, BN, WM, WN, AT, BT, LOAD, STORE>), dim3(unsigned(blocks)),
-                     dim3(64 * WM * WN), lds, s, a);
+  hipLaunchKernelGGL((k_gemm<E, BM, BN, WM, WN, LOAD, STORE>), dim3(unsigned(blocks)),
+                     dim3(Eng::NT), Eng::kLds, s, a);
   return hipGetLastError();
 }
 
-// The per-element MFMA chain does not depend on the tile shape, so the variants
-// below may use different tiles and still give the same bits.  The fp32
-// accumulator variants use a narrower tile to stay within the register file.
+// The per-element MFMA chain does not depend on the tile shape, so the GEMM
+// variants may use different tiles and still give the same bits.
+template <class E>
+hipError_t dx_dispatch(const GemmArgs& a, hipStream_t s);
+template <>
+hipError_t dx_dispatch<BF16>(const GemmArgs& a, hipStream_t s) {
+  return gemm_cfg<BF16, 256, 224, 2, 2, false, 0>(a, s);
+}
+template <>
+hipError_t dx_dispatch<F32>(const GemmArgs& a, hipStream_t s) {
+  return gemm_cfg<F32, 128, 128, 2, 2, false, 0>(a, s);
+}
+
 template <class E>
 hipError_t dw_dispatch(const GemmArgs& a, hipStream_t s);
-
 template <>
 hipError_t dw_dispatch<BF16>(const GemmArgs& a, hipStream_t s) {
   if (a.load_acc) {
-    if (a.store_acc) return gemm_cfg<BF16, 256, 128, 2, 2, false, false, true, 1>(a, s);
-    return gemm_cfg<BF16, 256, 128, 2, 2, false, false, true, 0>(a, s);
+    if (a.store_acc) return gemm_cfg<BF16, 256, 128, 2, 2, true, 1>(a, s);
+    return gemm_cfg<BF16, 256, 128, 2, 2, true, 0>(a, s);
   }
-  if (a.store_acc) return gemm_cfg<BF16, 256, 128, 2, 2, false, false, false, 1>(a, s);
-  return gemm_cfg<BF16, 256, 192, 2, 2, false, false, false, 0>(a, s);
+  if (a.store_acc) return gemm_cfg<BF16, 256, 224, 2, 2, false, 1>(a, s);
+  return gemm_cfg<BF16, 256, 224, 2, 2, false, 0>(a, s);
 }
-
 template <>
 hipError_t dw_dispatch<F32>(const GemmArgs& a, hipStream_t s) {
   if (a.load_acc) {
-    if (a.store_acc) return gemm_cfg<F32, 128, 128, 2, 2, false, false, true, 1>(a, s);
-    return gemm_cfg<F32, 128, 128, 2, 2, false, false, true, 0>(a, s);
+    if (a.store_acc) return gemm_cfg<F32, 128, 128, 2, 2, true, 1>(a, s);
+    return gemm_cfg<F32, 128, 128, 2, 2, true, 0>(a, s);
   }
-  if (a.store_acc) return gemm_cfg<F32, 128, 128, 2, 2, false, false, false, 1>(a, s);
-  return gemm_cfg<F32, 128, 128, 2, 2, false, false, false, 0>(a, s);
+  if (a.store_acc) return gemm_cfg<F32, 128, 128, 2, 2, false, 1>(a, s);
+  return gemm_cfg<F32, 128, 128, 2, 2, false, 0>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_forward(flp_dtype x, const FwdArgs& a, hipStream_t s) {
+  ProfScope ps(FLP_K_FORWARD, s);
   return x == FLP_BF16 ? fwd_dispatch<BF16>(a, s) : fwd_dispatch<F32>(a, s);
 }
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_merge, dim3(unsigned((a.N + 31) / 32)), dim3(256), 0, s, a);
+  ProfScope ps(FLP_K_MERGE, s);
+  hipLaunchKernelGGL(k_merge, dim3(unsigned((a.N + kMergeRows - 1) / kMergeRows)), dim3(256), 0, s,
+                     a);
   return hipGetLastError();
 }
 
 hipError_t launch_dz(flp_dtype x, const DzArgs& a, hipStream_t s) {
-  return x == FLP_BF16 ? dz_dispatch<BF16>(a, s) : dz_dispatch<F32>(a, s);
+  ProfScope ps(FLP_K_DLOGITS, s);
+  if (x == FLP_BF16)
+    return odd_stages<BF16>(a.D) ? dz_cfg<BF16, int(kDzRowTile), 2, true>(a, s)
+                                 : dz_cfg<BF16, int(kDzRowTile), 2, false>(a, s);
+  return odd_stages<F32>(a.D) ? dz_cfg<F32, int(kDzRowTile), 2, true>(a, s)
+                              : dz_cfg<F32, int(kDzRowTile), 2, false>(a, s);
 }
 
 hipError_t launch_dx(flp_dtype x, const GemmArgs& a, hipStream_t s) {
-  if (x == FLP_BF16) return gemm_cfg<BF16, 256, 192, 2, 2, false, true, false, 0>(a, s);
-  return gemm_cfg<F32, 128, 128, 2, 2, false, true, false, 0>(a, s);
+  ProfScope ps(FLP_K_DHIDDEN, s);
+  return x == FLP_BF16 ? dx_dispatch<BF16>(a, s) : dx_dispatch<F32>(a, s);
 }
 
 hipError_t launch_dw(flp_dtype x, const GemmArgs& a, hipStream_t s) {
+  ProfScope ps(FLP_K_DWEIGHT, s);
   return x == FLP_BF16 ? dw_dispatch<BF16>(a, s) : dw_dispatch<F32>(a, s);
 }
 
 hipError_t launch_transpose(flp_dtype x, const void* src, int64_t rows, int64_t rows_pad, int64_t cols,
                             int64_t ld_src, void* dst, int64_t ld_dst, hipStream_t s) {
+  ProfScope ps(FLP_K_TRANSPOSE, s);
   const dim3 grid(unsigned((cols + 63) / 64), unsigned((rows_pad + 63) / 64));
   if (x == FLP_BF16)
     hipLaunchKernelGGL(k_transpose<uint16_t>, grid, dim3(256), 0, s,
@@ -854,16 +823,17 @@ hipError_t launch_transpose(flp_dtype x, const void* src, int64_t rows, int64_t 
 
 hipError_t launch_dbias_fold(const float* part, int64_t n_parts, int64_t ldz, int64_t V,
                              float* d_bias, int init, hipStream_t s) {
+  ProfScope ps(FLP_K_DBIAS, s);
   hipLaunchKernelGGL(k_dbias_fold, dim3(unsigned((V + 255) / 256)), dim3(256), 0, s, part, n_parts,
                      ldz, V, d_bias, init);
   return hipGetLastError();
 }
 
 const char* kernel_ids() {
-  return "k_fwd<bf16|f32, BM 32/64/128/256, BN 256, mfma_f32_16x16x32_bf16|16x16x4f32>; "
-         "k_merge<32 rows x 8 segments>; k_dz<BM 128, BN 256>; "
-         "k_gemm dX<256x192, W transposed in registers>; k_gemm dW<256x192, fp32 acc>; "
-         "k_transpose; k_dbias_fold";
+  return "engine: direct global->LDS (global_load_lds_dwordx4), ring of 4-5 LDS stages x 64 B of K, "
+         "mfma_f32_16x16x32_bf16 | 16x16x4f32; k_fwd<BM 32/64/128 x BN 256, 2x2 waves>; "
+         "k_merge<8 rows x 32 segments>; k_dz<BM 128 x BN 256>; k_gemm dX<256x224>; "
+         "k_gemm dW<256x224, fp32-acc variants 256x128>; k_transpose; k_dbias_fold";
 }
 
 }  // namespace flp

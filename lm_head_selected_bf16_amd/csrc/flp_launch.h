@@ -66,4 +66,13 @@ hipError_t launch_dbias_fold(const float* part, int64_t n_parts, int64_t ldz, in
                              float* d_bias, int init, hipStream_t s);
 const char* kernel_ids();
 
+// Event brackets around each launch while profiling is enabled (flp_api.cpp).
+struct ProfScope {
+  ProfScope(int kind, hipStream_t s);
+  ~ProfScope();
+  int kind;
+  hipStream_t stream;
+  hipEvent_t a = nullptr;
+};
+
 }  // namespace flp

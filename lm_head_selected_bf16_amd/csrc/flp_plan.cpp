@@ -85,6 +85,8 @@ BwdLayout bwd_layout_for_chunk(int64_t N, int64_t D, int64_t V, flp_dtype x, flp
   size_t off = 0;
   L.dz_off = off;
   if (need_dh) off += align_up(size_t(chunk) * size_t(L.ldz) * xs);
+  L.wt_off = off;  // W^T [D][ldz], zero-padded past V
+  if (need_dh) off += align_up(size_t(D) * size_t(L.ldz) * xs);
   L.dzt_off = off;
   if (need_dw) off += align_up(size_t(L.ldz) * size_t(chunk) * xs);
   L.ht_off = off;
@@ -109,9 +111,10 @@ BwdLayout bwd_layout_for_bytes(int64_t N, int64_t D, int64_t V, flp_dtype x, flp
   const size_t q = size_t(kRowQuantum);
   const size_t per_quantum = (need_dh ? q * ldz * xs : 0) + (need_dw ? q * (ldz + size_t(D)) * xs : 0) +
                              (need_db ? (q / size_t(kDzRowTile)) * ldz * 4 : 0);
-  const size_t fixed = (need_dw && dw != FLP_F32) ? align_up(size_t(V) * size_t(D) * 4) : 0;
+  const size_t fixed = ((need_dw && dw != FLP_F32) ? align_up(size_t(V) * size_t(D) * 4) : 0) +
+                       (need_dh ? align_up(size_t(D) * ldz * xs) : 0);
   int64_t nq = 0;
-  if (per_quantum > 0 && bytes > fixed + 5 * kAlign) nq = int64_t((bytes - fixed - 5 * kAlign) / per_quantum);
+  if (per_quantum > 0 && bytes > fixed + 6 * kAlign) nq = int64_t((bytes - fixed - 6 * kAlign) / per_quantum);
   nq = std::min<int64_t>(nq, full / kRowQuantum);
   for (; nq >= 1; --nq) {
     L = bwd_layout_for_chunk(N, D, V, x, dw, nq * kRowQuantum, need_dh, need_dw, need_db);

@@ -19,6 +19,8 @@ constexpr int64_t kVocabTile = 256;
 constexpr int64_t kRowQuantum = 256;
 // Row tile of the dlogits kernel: one d_bias partial row per tile.
 constexpr int64_t kDzRowTile = 128;
+// K of the d_weight GEMM (tokens) is padded with zeros to a multiple of this.
+constexpr int64_t kTokPad = 64;
 constexpr size_t kAlign = 256;
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -48,7 +50,7 @@ struct BwdLayout {
   int64_t n_chunks = 0;
   int64_t ldz = 0;        // row stride of dz in elements (V rounded up to kVocabTile)
   int64_t ldt = 0;        // row stride of dz^T and hidden^T in elements (= chunk)
-  size_t dz_off = 0, dzt_off = 0, ht_off = 0, dbp_off = 0, acc_off = 0, total = 0;
+  size_t dz_off = 0, wt_off = 0, dzt_off = 0, ht_off = 0, dbp_off = 0, acc_off = 0, total = 0;
   bool use_acc = false;   // fp32 d_weight accumulator in the workspace
 };
 // Size for a given chunk; need_* say which outputs are requested.
