@@ -309,7 +309,7 @@ struct Engine {
 // Workgroup = WM x 2 waves; wave (wm, wn) owns rows [wm*RW, wm*RW + RW) and the 128
 // vocabulary columns [wn*128, wn*128 + 128) of the BM x 256 tile.
 template <class E, int BM, int WM>
-using LogitEngine = Engine<E, BM, kTileCols, WM, 2, (BM <= 32 ? 4 : 5)>;
+using LogitEngine = Engine<E, BM, kTileCols, WM, 2, (BM <= 32 ? 4 : BM >= 256 ? 5 : 5)>;
 
 // The fixed per-row tree over the 32 values one lane holds of a wave's 128 columns.
 template <int WNB>
@@ -710,7 +710,8 @@ template <class E, bool ODD>
 hipError_t fwd_rows(const FwdArgs& a, hipStream_t s) {
   if (a.N <= 32) return fwd_cfg<E, 32, 2, ODD>(a, s);
   if (a.N <= 64) return fwd_cfg<E, 64, 2, ODD>(a, s);
-  return fwd_cfg<E, 128, 2, ODD>(a, s);
+  if (a.N <= 128) return fwd_cfg<E, 128, 2, ODD>(a, s);
+  return fwd_cfg<E, 256, 4, ODD>(a, s);
 }
 
 template <class E>
@@ -746,7 +747,7 @@ template <class E>
 hipError_t dx_dispatch(const GemmArgs& a, hipStream_t s);
 template <>
 hipError_t dx_dispatch<BF16>(const GemmArgs& a, hipStream_t s) {
-  return gemm_cfg<BF16, 256, 224, 2, 2, false, 0>(a, s);
+  return gemm_cfg<BF16, 256, 224, 4, 2, false, 0>(a, s);
 }
 template <>
 hipError_t dx_dispatch<F32>(const GemmArgs& a, hipStream_t s) {
@@ -758,11 +759,11 @@ hipError_t dw_dispatch(const GemmArgs& a, hipStream_t s);
 template <>
 hipError_t dw_dispatch<BF16>(const GemmArgs& a, hipStream_t s) {
   if (a.load_acc) {
-    if (a.store_acc) return gemm_cfg<BF16, 256, 128, 2, 2, true, 1>(a, s);
-    return gemm_cfg<BF16, 256, 128, 2, 2, true, 0>(a, s);
+    if (a.store_acc) return gemm_cfg<BF16, 256, 224, 4, 2, true, 1>(a, s);
+    return gemm_cfg<BF16, 256, 224, 4, 2, true, 0>(a, s);
   }
-  if (a.store_acc) return gemm_cfg<BF16, 256, 224, 2, 2, false, 1>(a, s);
-  return gemm_cfg<BF16, 256, 224, 2, 2, false, 0>(a, s);
+  if (a.store_acc) return gemm_cfg<BF16, 256, 224, 4, 2, false, 1>(a, s);
+  return gemm_cfg<BF16, 256, 224, 4, 2, false, 0>(a, s);
 }
 template <>
 hipError_t dw_dispatch<F32>(const GemmArgs& a, hipStream_t s) {
@@ -791,10 +792,10 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
 hipError_t launch_dz(flp_dtype x, const DzArgs& a, hipStream_t s) {
   ProfScope ps(FLP_K_DLOGITS, s);
   if (x == FLP_BF16)
-    return odd_stages<BF16>(a.D) ? dz_cfg<BF16, int(kDzRowTile), 2, true>(a, s)
-                                 : dz_cfg<BF16, int(kDzRowTile), 2, false>(a, s);
-  return odd_stages<F32>(a.D) ? dz_cfg<F32, int(kDzRowTile), 2, true>(a, s)
-                              : dz_cfg<F32, int(kDzRowTile), 2, false>(a, s);
+    return odd_stages<BF16>(a.D) ? dz_cfg<BF16, int(kDzRowTile), 4, true>(a, s)
+                                 : dz_cfg<BF16, int(kDzRowTile), 4, false>(a, s);
+  return odd_stages<F32>(a.D) ? dz_cfg<F32, int(kDzRowTile), 4, true>(a, s)
+                              : dz_cfg<F32, int(kDzRowTile), 4, false>(a, s);
 }
 
 hipError_t launch_dx(flp_dtype x, const GemmArgs& a, hipStream_t s) {
@@ -831,9 +832,9 @@ hipError_t launch_dbias_fold(const float* part, int64_t n_parts, int64_t ldz, in
 
 const char* kernel_ids() {
   return "engine: direct global->LDS (global_load_lds_dwordx4), ring of 4-5 LDS stages x 64 B of K, "
-         "mfma_f32_16x16x32_bf16 | 16x16x4f32; k_fwd<BM 32/64/128 x BN 256, 2x2 waves>; "
-         "k_merge<8 rows x 32 segments>; k_dz<BM 128 x BN 256>; k_gemm dX<256x224>; "
-         "k_gemm dW<256x224, fp32-acc variants 256x128>; k_transpose; k_dbias_fold";
+         "mfma_f32_16x16x32_bf16 | 16x16x4f32; k_fwd<BM 32/64/128 x BN 256 2x2 waves, BM 256 4x2 waves>; "
+         "k_merge<8 rows x 32 segments>; k_dz<BM 256 x BN 256, 4x2 waves>; k_gemm dX<256x224, 4x2 waves>; "
+         "k_gemm dW<256x224, 4x2 waves>; k_transpose; k_dbias_fold";
 }
 
 }  // namespace flp

@@ -18,7 +18,7 @@ constexpr int64_t kVocabTile = 256;
 // Row granularity of backward chunks (multiple of every row tile and K step).
 constexpr int64_t kRowQuantum = 256;
 // Row tile of the dlogits kernel: one d_bias partial row per tile.
-constexpr int64_t kDzRowTile = 128;
+constexpr int64_t kDzRowTile = 256;
 // K of the d_weight GEMM (tokens) is padded with zeros to a multiple of this.
 constexpr int64_t kTokPad = 64;
 constexpr size_t kAlign = 256;
