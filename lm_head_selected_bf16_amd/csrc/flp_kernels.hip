@@ -119,17 +119,20 @@ __device__ __forceinline__ int64_t load_target(const void* t, int t64, int64_t i
 // Workgroup id -> (row tile, column tile).  Workgroups are dispatched
 // round-robin over the 8 XCDs, so ids are first regrouped so that each XCD
 // receives a contiguous run of logical tiles (sharing its L2), then the run is
-// walked in groups of kGroupM row tiles, row tile fastest, so that the
-// workgroups resident at one time share both operand tiles.
+// walked in groups of GM row tiles, row tile fastest, so that the workgroups
+// resident at one time share both operand tiles.  Logits tiles use GM = 8
+// (8 row tiles x 4 vocabulary tiles per XCD at a time); the backward GEMMs use
+// GM = 4 (measured best of 2, 4 and 8 for their 12 column tiles).
+template <int GM = kGroupM>
 __device__ __forceinline__ void tile_of(int bid, int nbm, int nbn, int& tm, int& tn) {
   const int total = nbm * nbn;
   const int per = total >> 3;
   int lin = bid;
   if (bid < per * 8) lin = (bid & 7) * per + (bid >> 3);
-  const int width = kGroupM * nbn;
+  const int width = GM * nbn;
   const int grp = lin / width;
-  const int first = grp * kGroupM;
-  const int gm = min(nbm - first, kGroupM);
+  const int first = grp * GM;
+  const int gm = min(nbm - first, GM);
   const int in = lin - grp * width;
   tm = first + in % gm;
   tn = in / gm;
@@ -277,13 +280,15 @@ struct Engine {
       const int rd = st + 1 < nst ? st + 1 : st;
       read(nxt, smem + (rd % NS) * kSlots, fa, fb);
       mmas(acc, cur);
-      // Keep the reads of stage st + 1 spread among the MFMAs of stage st.
+      // Keep the reads of stage st + 1 spread among the MFMAs of stage st, starting
+      // with MFMAs: the wait for this stage's fragments then precedes every new read
+      // (LDS reads complete in order, so a read issued first would be waited for too).
       constexpr int kR = WMB + WNB, kM = WMB * WNB * (E::kSize == 2 ? 1 : 4);
       constexpr int kStep = kM / kR > 0 ? kM / kR : 1;
 #pragma unroll
       for (int k = 0; k < kR; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, kStep, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x008, kM - kStep * kR, 0);
     };
@@ -309,7 +314,7 @@ struct Engine {
 // Workgroup = WM x 2 waves; wave (wm, wn) owns rows [wm*RW, wm*RW + RW) and the 128
 // vocabulary columns [wn*128, wn*128 + 128) of the BM x 256 tile.
 template <class E, int BM, int WM>
-using LogitEngine = Engine<E, BM, kTileCols, WM, 2, (BM <= 32 ? 4 : BM >= 256 ? 5 : 5)>;
+using LogitEngine = Engine<E, BM, kTileCols, WM, 2, (BM <= 32) ? 4 : 5>;
 
 // The fixed per-row tree over the 32 values one lane holds of a wave's 128 columns.
 template <int WNB>
@@ -608,14 +613,14 @@ __global__ __launch_bounds__(128 * WM) void k_dz(DzArgs p) {
 // 1 = fp32 to p.acc.
 template <class E, int BM, int BN, int WM, int WN, bool LOAD, int STORE>
 __global__ __launch_bounds__(64 * WM * WN) void k_gemm(GemmArgs p) {
-  using Eng = Engine<E, BM, BN, WM, WN, 5>;
+  using Eng = Engine<E, BM, BN, WM, WN, 4>;
   constexpr int RW = Eng::RW, CW = Eng::CW, WMB = Eng::WMB, WNB = Eng::WNB;
   extern __shared__ u32x4 smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % WM, wn = wave / WM, i = lane & 15, g = lane >> 4;
   const int nbm = int((p.M + BM - 1) / BM), nbn = int((p.N + BN - 1) / BN);
   int tm, tn;
-  tile_of(blockIdx.x, nbm, nbn, tm, tn);
+  tile_of<4>(blockIdx.x, nbm, nbn, tm, tn);
   const int64_t m0 = int64_t(tm) * BM, n0 = int64_t(tn) * BN;
   const int64_t nl = n0 + wn * CW + 4 * g;
 
@@ -732,7 +737,7 @@ hipError_t dz_cfg(const DzArgs& a, hipStream_t s) {
 
 template <class E, int BM, int BN, int WM, int WN, bool LOAD, int STORE>
 hipError_t gemm_cfg(const GemmArgs& a, hipStream_t s) {
-  using Eng = Engine<E, BM, BN, WM, WN, 5>;
+  using Eng = Engine<E, BM, BN, WM, WN, 4>;
   static hipError_t once = prepare(k_gemm<E, BM, BN, WM, WN, LOAD, STORE>, Eng::kLds);
   if (once != hipSuccess) return once;
   const int64_t blocks = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
