@@ -474,25 +474,25 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs p) {
 // ([vocab][token], for d_weight = dz^T hidden) so that both GEMMs read
 // K-contiguous operands.  The transposed copy goes through LDS in passes of
 // CPP columns so that every vocabulary row receives BM contiguous tokens.
-// LDS staging of the transposed tile (bf16): [256 columns][BM tokens], each
-// column row padded by 16 bytes.
-template <int BM>
-struct DzT {
-  static constexpr int kRowB = BM * 2 + 16;
+// LDS staging of a bf16 [256 x 256] tile of dz for coalesced stores: 256 rows of
+// 512 bytes, each padded by 16 bytes.  Used twice: once token-major (dz rows),
+// once column-major (dz^T rows).
+struct DzStage {
+  static constexpr int kRowB = kTileCols * 2 + 16;
   static constexpr size_t kBytes = size_t(kTileCols) * kRowB;
 };
 
 template <class E, int BM, int WM>
 constexpr size_t dz_lds() {
   using Eng = LogitEngine<E, BM, WM>;
-  return (E::kSize == 2 && DzT<BM>::kBytes > Eng::kLds) ? DzT<BM>::kBytes : Eng::kLds;
+  return (E::kSize == 2 && DzStage::kBytes > Eng::kLds) ? DzStage::kBytes : Eng::kLds;
 }
 
 template <class E, int BM, int WM, bool ODD>
 __global__ __launch_bounds__(128 * WM) void k_dz(DzArgs p) {
   using Eng = LogitEngine<E, BM, WM>;
   constexpr int RW = Eng::RW, WMB = Eng::WMB, WNB = Eng::WNB, NT = Eng::NT;
-  constexpr bool kStageT = E::kSize == 2;  // bf16: transpose through LDS
+  constexpr bool kStage = E::kSize == 2 && BM == kTileCols;  // bf16: coalesce through LDS
   extern __shared__ u32x4 smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % WM, wn = wave / WM, i = lane & 15, g = lane >> 4;
@@ -516,67 +516,118 @@ __global__ __launch_bounds__(128 * WM) void k_dz(DzArgs p) {
   const int64_t cw = col0 + wn * kHalfCols;
   const int64_t vlim = p.V - cw;
   char* lds = reinterpret_cast<char*>(smem);
-  float bcol[WNB][4];
   f32x4_t csum[WNB];
-#pragma unroll
-  for (int nb = 0; nb < WNB; ++nb) {
-    csum[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t c = cw + nb * 16 + 4 * g + r;
-      bcol[nb][r] = (p.bias != nullptr && c < p.V) ? p.bias[c] : 0.f;
-    }
-  }
-#pragma unroll
-  for (int mb = 0; mb < WMB; ++mb) {
-    const int tl = wm * RW + mb * 16 + i;  // token within the tile
-    const int64_t row = row0 + tl;
-    const bool rv = row < p.rows;
-    const float invT = (p.temperature != nullptr && rv) ? 1.0f / p.temperature[row] : 1.0f;
-    const int64_t t = rv ? load_target(p.targets, p.t64, row) : -1;
-    const bool valid = t >= 0 && t < p.V;
-    const float G = valid ? p.grad_out[row] * invT : 0.f;
-    const float L = rv ? p.lse[row] : 0.f;
-    const int64_t trel = t - cw;
+  {
+    float bcol[WNB][4];
 #pragma unroll
     for (int nb = 0; nb < WNB; ++nb) {
-      f32x4_t d;
+      csum[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int cl = nb * 16 + 4 * g + r;
-        const float z = (acc[mb][nb][r] + bcol[nb][r]) * invT;
-        const float pr = fast_exp2((z - L) * kLog2e);
-        const float oh = (cl == trel) ? 1.0f : 0.0f;
-        float v = G * (oh - pr);
-        v = (valid && cl < vlim) ? v : 0.0f;
-        d[r] = v;
+        const int64_t c = cw + nb * 16 + 4 * g + r;
+        bcol[nb][r] = (p.bias != nullptr && c < p.V) ? p.bias[c] : 0.f;
       }
-      csum[nb] += d;
-      if (p.dz != nullptr) store4<E>(p.dz, row * p.ldz + cw + nb * 16 + 4 * g, d);
-      if (p.dzT != nullptr) {
-        const int cl = wn * kHalfCols + nb * 16 + 4 * g;  // column within the tile
-        if (kStageT) {
+    }
+    // dz = G (onehot - exp(z - lse)) / T, kept in the accumulator registers.
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            reinterpret_cast<uint16_t*>(lds + (cl + r) * DzT<BM>::kRowB)[tl] =
-                uint16_t(bf16_bits_rne(d[r]));
+    for (int mb = 0; mb < WMB; ++mb) {
+      const int64_t row = row0 + wm * RW + mb * 16 + i;
+      const bool rv = row < p.rows;
+      const float invT = (p.temperature != nullptr && rv) ? 1.0f / p.temperature[row] : 1.0f;
+      const int64_t t = rv ? load_target(p.targets, p.t64, row) : -1;
+      const bool valid = t >= 0 && t < p.V;
+      const float G = valid ? p.grad_out[row] * invT : 0.f;
+      const float L = rv ? p.lse[row] : 0.f;
+      const int64_t trel = t - cw;
+#pragma unroll
+      for (int nb = 0; nb < WNB; ++nb) {
+        f32x4_t d;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int cl = nb * 16 + 4 * g + r;
+          const float z = (acc[mb][nb][r] + bcol[nb][r]) * invT;
+          const float pr = fast_exp2((z - L) * kLog2e);
+          const float oh = (cl == trel) ? 1.0f : 0.0f;
+          float v = G * (oh - pr);
+          v = (valid && cl < vlim) ? v : 0.0f;
+          d[r] = v;
+        }
+        csum[nb] += d;
+        if constexpr (kStage) {
+          acc[mb][nb] = d;
         } else {
+          if (p.dz != nullptr) store4<E>(p.dz, row * p.ldz + cw + nb * 16 + 4 * g, d);
+          if (p.dzT != nullptr) {
+            const int cl = wn * kHalfCols + nb * 16 + 4 * g;  // column within the tile
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            reinterpret_cast<float*>(p.dzT)[(col0 + cl + r) * p.ldt + row] = d[r];
+            for (int r = 0; r < 4; ++r) {
+              if (E::kSize == 4)
+                reinterpret_cast<float*>(p.dzT)[(col0 + cl + r) * p.ldt + row] = d[r];
+              else
+                reinterpret_cast<uint16_t*>(p.dzT)[(col0 + cl + r) * p.ldt + row] =
+                    uint16_t(bf16_bits_rne(d[r]));
+            }
+          }
         }
       }
     }
   }
-  if (kStageT && p.dzT != nullptr) {
-    // Every vocabulary row of dz^T receives the tile's BM contiguous tokens.
-    constexpr int kChunksPerCol = BM * 2 / 16;
-    __syncthreads();
-    for (int idx = tid; idx < kTileCols * kChunksPerCol; idx += NT) {
-      const int c = idx / kChunksPerCol, ch = idx % kChunksPerCol;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(lds + c * DzT<BM>::kRowB + ch * 16);
-      *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.dzT) + (col0 + c) * p.ldt + row0 +
-                                ch * 8) = v;
+  if constexpr (kStage) {
+    constexpr int kRowB = DzStage::kRowB;
+    constexpr int kChunks = kTileCols * (kTileCols * 2 / 16);  // 16-byte chunks per tile
+    if (p.dz != nullptr) {
+      // Token-major tile: each lane writes its 4 consecutive columns (8 bytes).
+#pragma unroll
+      for (int mb = 0; mb < WMB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < WNB; ++nb) {
+          const int tl = wm * RW + mb * 16 + i;
+          const int cl = wn * kHalfCols + nb * 16 + 4 * g;
+          u32x2 w;
+          w.x = bf16_bits_rne(acc[mb][nb][0]) | (bf16_bits_rne(acc[mb][nb][1]) << 16);
+          w.y = bf16_bits_rne(acc[mb][nb][2]) | (bf16_bits_rne(acc[mb][nb][3]) << 16);
+          *reinterpret_cast<u32x2*>(lds + tl * kRowB + cl * 2) = w;
+        }
+      __syncthreads();
+      for (int idx = tid; idx < kChunks; idx += NT) {
+        const int tl = idx >> 5, ch = idx & 31;
+        const int64_t row = row0 + tl;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(lds + tl * kRowB + ch * 16);
+        if (row < p.rows)
+          *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.dz) + row * p.ldz + col0 + ch * 8) = v;
+      }
+      __syncthreads();
+    }
+    if (p.dzT != nullptr) {
+      // Column-major tile.  Lanes i and i ^ 1 hold adjacent tokens; after swapping
+      // two values, the even lane writes columns c, c+1 and the odd lane columns
+      // c+2, c+3, each as one 4-byte (token, token + 1) pair.
+      const bool even = (i & 1) == 0;
+#pragma unroll
+      for (int mb = 0; mb < WMB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < WNB; ++nb) {
+          const f32x4_t d = acc[mb][nb];
+          const float x0 = even ? d[2] : d[0];
+          const float x1 = even ? d[3] : d[1];
+          const float y0 = __shfl_xor(x0, 1);
+          const float y1 = __shfl_xor(x1, 1);
+          const int te = wm * RW + mb * 16 + (i & ~1);  // even token of the pair
+          const int c = wn * kHalfCols + nb * 16 + 4 * g + (even ? 0 : 2);
+          const float lo0 = even ? d[0] : y0, hi0 = even ? y0 : d[2];
+          const float lo1 = even ? d[1] : y1, hi1 = even ? y1 : d[3];
+          *reinterpret_cast<uint32_t*>(lds + c * kRowB + te * 2) =
+              bf16_bits_rne(lo0) | (bf16_bits_rne(hi0) << 16);
+          *reinterpret_cast<uint32_t*>(lds + (c + 1) * kRowB + te * 2) =
+              bf16_bits_rne(lo1) | (bf16_bits_rne(hi1) << 16);
+        }
+      __syncthreads();
+      for (int idx = tid; idx < kChunks; idx += NT) {
+        const int cl = idx >> 5, ch = idx & 31;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(lds + cl * kRowB + ch * 16);
+        *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.dzT) + (col0 + cl) * p.ldt + row0 +
+                                  ch * 8) = v;
+      }
     }
   }
   if (p.dbias_part == nullptr) return;
