@@ -16,11 +16,11 @@
 // One MFMA engine serves all four contractions.  Every operand is stored
 // K-contiguous (W is transposed once per backward for d_hidden; hidden per
 // chunk for d_weight) and streamed by direct global->LDS loads
-// (global_load_lds_dwordx4, no register staging) into two LDS stages of
-// 128 bytes of K per row.  Waves form a WM x WN grid; each wave owns a
-// (BM/WM) x (BN/WN) block of 16 x 16 MFMA tiles with its fp32 accumulators in
-// AGPRs, and double-buffers its operand fragments across the two 64-byte
-// halves of a stage.
+// (global_load_lds_dwordx4, no register staging, whole 128-byte lines) into two
+// LDS stages of 128 bytes of K per row.  Waves form a WM x WN grid; each wave
+// owns a (BM/WM) x (BN/WN) block of 16 x 16 MFMA tiles with fp32 accumulators,
+// and double-buffers its operand fragments across the two 64-byte halves of a
+// stage.
 //
 // Register layout: every MFMA is issued as mfma(A = N-side fragment,
 // B = M-side fragment), so lane l holds output row (l % 16) of a 16-row block
@@ -61,12 +61,6 @@ struct BF16 {
 struct F32 {
   static constexpr int kSize = 4;
 };
-
-// LDS tiles hold rows of 4 16-byte chunks (one 64-byte stage of K).  Chunk c
-// of row r lives at chunk position c ^ ((r >> 2) & 3).  (A wave64 ds_read_b128
-// costs the same for every 16-byte-aligned pattern measured on gfx950; the
-// swizzle only keeps each 16-row fragment read spread over all positions.)
-__device__ __forceinline__ int swzf(int r) { return (r >> 2) & 3; }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -140,21 +134,24 @@ __device__ __forceinline__ void tile_of(int bid, int nbm, int nbn, int& tm, int&
 
 // ---- direct global -> LDS staging of one operand tile --------------------------------------
 //
-// ROWS rows x 64 bytes per stage.  One wave instruction fills 64 consecutive
-// 16-byte LDS slots (lane i -> slot base + i): instruction inst covers rows
-// 16*inst + lane / 4, chunk position lane % 4, i.e. logical chunk
-// (lane % 4) ^ ((lane >> 4) & 3).  Rows past the end of the operand read a
-// clamped (valid) row whose results are never used.
+// A pipeline stage holds 128 bytes of K per operand row (two 64-byte MFMA steps),
+// so that every load covers whole 128-byte cache lines.  In LDS a row is 8
+// 16-byte chunks; logical chunk c of row r sits at position c ^ ((r >> 1) & 7),
+// which puts the 16 rows of a fragment read on 16 distinct bank groups.  One wave
+// instruction fills 64 consecutive LDS chunks (lane l -> chunk base + l): it
+// covers rows 8 inst + l / 8 at positions l % 8.  Rows past the end of the
+// operand read a clamped (valid) row whose results are never used; in a last,
+// half stage (64 bytes of K left) the upper four chunks repeat the lower four.
 template <int ROWS, int NW>
 struct DTile {
-  static constexpr int kInsts = ROWS / 16;
+  static constexpr int kInsts = ROWS / 8;
   static constexpr int kPer = (kInsts + NW - 1) / NW;
   // Wave w issues instructions w*kPer .. min(kInsts, (w+1)*kPer) - 1, so the last
   // waves may issue fewer; kMin is the fewest any wave issues per stage.
   static constexpr int kMin = kInsts - (NW - 1) * kPer > 0 ? kInsts - (NW - 1) * kPer : 0;
   static_assert(ROWS % 16 == 0, "tile rows must be a multiple of 16");
-  uint32_t q, voff;     // q = lane / 4; voff = q * ld + chunk * 16
-  uint32_t coff;
+  int q;                // row within the instruction's 8 rows
+  int c0, c1;           // logical chunk loaded by this lane for even / odd instructions
   int64_t ld, rows_valid;
   bool full;            // every row of the tile is valid: no clamping
 
@@ -162,24 +159,22 @@ struct DTile {
     ld = ld_;
     rows_valid = rows_valid_;
     full = rows_valid_ >= ROWS;
-    q = uint32_t(lane >> 2);
-    coff = uint32_t(((lane & 3) ^ ((lane >> 4) & 3)) * 16);
-    voff = uint32_t(int64_t(q) * ld_) + coff;
+    q = lane >> 3;
+    c0 = (lane & 7) ^ (q >> 1);
+    c1 = c0 ^ 4;
   }
-  __device__ __forceinline__ void issue(const char* base, uint32_t kb0, u32x4* lds, int wave) const {
-    const char* sb = base + kb0;
+  __device__ __forceinline__ void issue(const char* base, int stage, bool half, u32x4* lds,
+                                        int wave) const {
+    const char* sb = base + int64_t(stage) * 128;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int inst = wave * kPer + j;
       if (kInsts % NW == 0 || inst < kInsts) {
-        uint32_t off;
-        if (full) {
-          off = uint32_t(inst * 16) * uint32_t(ld) + voff;
-        } else {
-          int64_t r = int64_t(inst) * 16 + q;
-          r = r < rows_valid ? r : rows_valid - 1;
-          off = uint32_t(r * ld) + coff;
-        }
+        int c = (inst & 1) ? c1 : c0;
+        c = half ? (c & 3) : c;
+        int64_t r = int64_t(inst) * 8 + q;
+        if (!full) r = r < rows_valid ? r : rows_valid - 1;
+        const uint32_t off = uint32_t(r * ld) + uint32_t(c * 16);
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(sb + off),
                                          (__attribute__((address_space(3))) void*)(lds + inst * 64),
                                          16, 0, 0);
@@ -188,19 +183,23 @@ struct DTile {
   }
 };
 
-// Wait until at most N of this wave's vector-memory loads are outstanding, then
-// barrier the workgroup.  The direct loads complete in issue order.
+// Wait until at most N of this wave's vector-memory loads are outstanding and its
+// LDS reads have completed, then barrier the workgroup.  The direct loads
+// complete in issue order.
 template <int N>
-__device__ __forceinline__ void wait_loads_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+__device__ __forceinline__ void wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
 // ---- the MFMA engine -------------------------------------------------------------------------
 //
-// A ring of NS LDS stages; stage s of K lives in buffer s % NS.  Loads of stage
-// s + NS - 1 are issued while stage s is multiplied, and the fragments of stage
-// s + 1 are read from LDS in between the MFMAs of stage s.
-template <class E, int BM, int BN, int WM, int WN, int NS>
+// Two LDS buffers of one 128-byte stage each; stage t lives in buffer t % 2 and
+// holds the MFMA steps 2t (chunks 0-3) and 2t + 1 (chunks 4-7).  Every MFMA step
+// multiplies fragments read from LDS during the previous step.  The workgroup
+// synchronises once per stage, between its two steps: stage t + 1 must have
+// landed (its loads were issued one stage earlier) and every wave must be done
+// reading stage t, whose buffer then receives the loads of stage t + 2.
+template <class E, int BM, int BN, int WM, int WN>
 struct Engine {
   static constexpr int NW = WM * WN;
   static constexpr int NT = 64 * NW;
@@ -208,28 +207,25 @@ struct Engine {
   static constexpr int CW = BN / WN;
   static constexpr int WMB = RW / 16;
   static constexpr int WNB = CW / 16;
-  static constexpr int kSlots = (BM + BN) * 4;  // 16-byte LDS slots per stage
-  static constexpr size_t kStage = size_t(kSlots) * 16;
-  static constexpr size_t kLds = NS * kStage;
-  // Loads per stage of the wave that issues the fewest.  Waiting until at most
-  // k * kLoads loads are outstanding therefore guarantees, for every wave, that
-  // all but its last k stages have landed (waves with more loads wait a little
-  // longer than needed).
+  static constexpr int kSlots = (BM + BN) * 8;  // 16-byte LDS chunks per stage
+  static constexpr size_t kLds = 2 * size_t(kSlots) * 16;
+  // Loads per stage of the wave that issues the fewest: waiting until at most
+  // kLoads are outstanding guarantees, for every wave, that all but its last
+  // stage have landed.
   static constexpr int kLoads = DTile<BM, NW>::kMin + DTile<BN, NW>::kMin;
   static_assert(RW % 16 == 0 && CW % 16 == 0, "wave tile must be a multiple of 16");
-  static_assert(NS >= 3, "the ring needs at least three stages");
 
   struct Frag {
     u32x4 a[WMB], b[WNB];
   };
 
-  // Fragments of the stage at slot offset `st`: per-lane base slots fa, fb; the
-  // 16-row blocks are immediate offsets (64 slots apart).
+  // Fragments of one MFMA step from the buffer at `st`: per-lane base chunks fa,
+  // fb; the 16-row blocks are immediate offsets (128 chunks apart).
   __device__ __forceinline__ static void read(Frag& f, const u32x4* st, int fa, int fb) {
 #pragma unroll
-    for (int mb = 0; mb < WMB; ++mb) f.a[mb] = st[fa + mb * 64];
+    for (int mb = 0; mb < WMB; ++mb) f.a[mb] = st[fa + mb * 128];
 #pragma unroll
-    for (int nb = 0; nb < WNB; ++nb) f.b[nb] = st[BM * 4 + fb + nb * 64];
+    for (int nb = 0; nb < WNB; ++nb) f.b[nb] = st[BM * 8 + fb + nb * 128];
   }
 
   __device__ __forceinline__ static void mmas(f32x4_t (&acc)[WMB][WNB], const Frag& f) {
@@ -237,6 +233,21 @@ struct Engine {
     for (int mb = 0; mb < WMB; ++mb)
 #pragma unroll
       for (int nb = 0; nb < WNB; ++nb) mma64<E>(acc[mb][nb], f.b[nb], f.a[mb]);
+  }
+
+  // Keep the reads of the next step spread among the MFMAs of this one, starting
+  // with MFMAs: the wait for this step's fragments then precedes every new read
+  // (LDS reads complete in order, so a read issued first would be waited for too).
+  __device__ __forceinline__ static void interleave() {
+    constexpr int kR = WMB + WNB, kM = WMB * WNB * (E::kSize == 2 ? 1 : 4);
+    constexpr int kStep = kM / kR > 0 ? kM / kR : 1;
+#pragma unroll
+    for (int k = 0; k < kR; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, kStep, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kM - kStep * kR, 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // acc (+)= A[rows, K] . B[rows, K]^T over kbytes of K (a multiple of 64; ODD when
@@ -248,64 +259,55 @@ struct Engine {
                                              int64_t b_rows_valid, int64_t kbytes, u32x4* smem) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave % WM, wn = wave / WM, i = lane & 15, g = lane >> 4;
-    const int nst = int(kbytes / kStageBytes);
+    const int nsteps = int(kbytes / kStageBytes);
+    const int nst = (nsteps + 1) / 2;
     DTile<BM, NW> ta;
     DTile<BN, NW> tb;
     ta.init(lda, a_rows_valid, lane);
     tb.init(ldb, b_rows_valid, lane);
-    const int pos = g ^ swzf(i);
-    const int fa = (wm * RW + i) * 4 + pos;
-    const int fb = (wn * CW + i) * 4 + pos;
-    auto issue = [&](int st) {
-      u32x4* dst = smem + (st % NS) * kSlots;
-      ta.issue(a, uint32_t(st) * kStageBytes, dst, wave);
-      tb.issue(b, uint32_t(st) * kStageBytes, dst + BM * 4, wave);
+    // Chunk of the even step for this lane; the odd step's is pos ^ 4.
+    const int pos = g ^ ((i >> 1) & 7);
+    const int fa = (wm * RW + i) * 8 + pos;
+    const int fb = (wn * CW + i) * 8 + pos;
+    auto issue = [&](int t) {
+      u32x4* dst = smem + (t & 1) * kSlots;
+      const bool half = ODD && t == nst - 1;
+      ta.issue(a, t, half, dst, wave);
+      tb.issue(b, t, half, dst + BM * 8, wave);
     };
-#pragma unroll
-    for (int st = 0; st < NS - 1; ++st)
-      if (st < nst) issue(st);
-    if (nst > NS - 2)
-      wait_loads_barrier<kLoads * (NS - 2)>();
-    else
-      wait_loads_barrier<0>();
-    // One step: wait for stage st + 1, refill the ring, read st + 1 into `nxt` while
-    // multiplying stage st from `cur`.  The last step re-reads the last stage
-    // (unused) so that every step has the same straight-line body.
-    auto step = [&](int st, const Frag& cur, Frag& nxt) {
-      if (st + NS - 1 < nst)
-        wait_loads_barrier<kLoads * (NS - 3)>();
-      else
-        wait_loads_barrier<0>();
-      if (st + NS - 1 < nst) issue(st + NS - 1);  // into the buffer of stage st - 1
-      const int rd = st + 1 < nst ? st + 1 : st;
-      read(nxt, smem + (rd % NS) * kSlots, fa, fb);
-      mmas(acc, cur);
-      // Keep the reads of stage st + 1 spread among the MFMAs of stage st, starting
-      // with MFMAs: the wait for this stage's fragments then precedes every new read
-      // (LDS reads complete in order, so a read issued first would be waited for too).
-      constexpr int kR = WMB + WNB, kM = WMB * WNB * (E::kSize == 2 ? 1 : 4);
-      constexpr int kStep = kM / kR > 0 ? kM / kR : 1;
-#pragma unroll
-      for (int k = 0; k < kR; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, kStep, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, kM - kStep * kR, 0);
-    };
+    issue(0);
+    if (nst > 1) {
+      issue(1);
+      wait_barrier<kLoads>();
+    } else {
+      wait_barrier<0>();
+    }
     Frag f0, f1;
     read(f0, smem, fa, fb);
-    if constexpr (!ODD) {
-      for (int st = 0; st < nst; st += 2) {
-        step(st, f0, f1);
-        step(st + 1, f1, f0);
+    // Stage t: step 2t from f0 (read one step earlier) while reading step 2t + 1
+    // into f1; synchronise; step 2t + 1 from f1 while reading step 2t + 2 into
+    // f0.  After the last stage a valid step is re-read so that the body stays
+    // straight-line.
+    auto stage = [&](int t) {
+      const u32x4* cur = smem + (t & 1) * kSlots;
+      read(f1, cur, fa ^ 4, fb ^ 4);
+      mmas(acc, f0);
+      interleave();
+      const bool more = t + 1 < nst;
+      if (more) {
+        wait_barrier<0>();
+        if (t + 2 < nst) issue(t + 2);
       }
-    } else {
-      step(0, f0, f1);
-      for (int st = 1; st < nst; st += 2) {
-        step(st, f1, f0);
-        step(st + 1, f0, f1);
-      }
-    }
+      if (more)
+        read(f0, smem + ((t + 1) & 1) * kSlots, fa, fb);
+      else
+        read(f0, cur, fa ^ 4, fb ^ 4);
+      mmas(acc, f1);
+      interleave();
+    };
+    const int nfull = ODD ? nst - 1 : nst;
+    for (int t = 0; t < nfull; ++t) stage(t);
+    if constexpr (ODD) mmas(acc, f0);
   }
 };
 
@@ -314,7 +316,7 @@ struct Engine {
 // Workgroup = WM x 2 waves; wave (wm, wn) owns rows [wm*RW, wm*RW + RW) and the 128
 // vocabulary columns [wn*128, wn*128 + 128) of the BM x 256 tile.
 template <class E, int BM, int WM>
-using LogitEngine = Engine<E, BM, kTileCols, WM, 2, (BM <= 32) ? 4 : 5>;
+using LogitEngine = Engine<E, BM, kTileCols, WM, 2>;
 
 // The fixed per-row tree over the 32 values one lane holds of a wave's 128 columns.
 template <int WNB>
@@ -664,7 +666,7 @@ __global__ __launch_bounds__(128 * WM) void k_dz(DzArgs p) {
 // 1 = fp32 to p.acc.
 template <class E, int BM, int BN, int WM, int WN, bool LOAD, int STORE>
 __global__ __launch_bounds__(64 * WM * WN) void k_gemm(GemmArgs p) {
-  using Eng = Engine<E, BM, BN, WM, WN, 4>;
+  using Eng = Engine<E, BM, BN, WM, WN>;
   constexpr int RW = Eng::RW, CW = Eng::CW, WMB = Eng::WMB, WNB = Eng::WNB;
   extern __shared__ u32x4 smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -788,7 +790,7 @@ hipError_t dz_cfg(const DzArgs& a, hipStream_t s) {
 
 template <class E, int BM, int BN, int WM, int WN, bool LOAD, int STORE>
 hipError_t gemm_cfg(const GemmArgs& a, hipStream_t s) {
-  using Eng = Engine<E, BM, BN, WM, WN, 4>;
+  using Eng = Engine<E, BM, BN, WM, WN>;
   static hipError_t once = prepare(k_gemm<E, BM, BN, WM, WN, LOAD, STORE>, Eng::kLds);
   if (once != hipSuccess) return once;
   const int64_t blocks = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
