@@ -286,22 +286,18 @@ struct Engine {
     read(f0, smem, fa, fb);
     // Stage t: step 2t from f0 (read one step earlier) while reading step 2t + 1
     // into f1; synchronise; step 2t + 1 from f1 while reading step 2t + 2 into
-    // f0.  After the last stage a valid step is re-read so that the body stays
-    // straight-line.
+    // f0.  After the last stage the other buffer still holds consumed data that
+    // no load overwrites any more; reading it (unused) keeps the body free of
+    // branches around the fragment reads.
     auto stage = [&](int t) {
-      const u32x4* cur = smem + (t & 1) * kSlots;
-      read(f1, cur, fa ^ 4, fb ^ 4);
+      read(f1, smem + (t & 1) * kSlots, fa ^ 4, fb ^ 4);
       mmas(acc, f0);
       interleave();
-      const bool more = t + 1 < nst;
-      if (more) {
+      if (t + 1 < nst) {
         wait_barrier<0>();
         if (t + 2 < nst) issue(t + 2);
       }
-      if (more)
-        read(f0, smem + ((t + 1) & 1) * kSlots, fa, fb);
-      else
-        read(f0, cur, fa ^ 4, fb ^ 4);
+      read(f0, smem + ((t + 1) & 1) * kSlots, fa, fb);
       mmas(acc, f1);
       interleave();
     };
