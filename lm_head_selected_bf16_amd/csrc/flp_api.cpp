@@ -158,7 +158,7 @@ flp_status flp_backward(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
   void* dz = d_hidden ? at(workspace, L.dz_off) : nullptr;
   void* wT = d_hidden ? at(workspace, L.wt_off) : nullptr;
   if (d_hidden &&
-      launch_transpose(x_dtype, weight, V, L.ldz, D, D, wT, L.ldz, s) != hipSuccess)
+      launch_transpose(x_dtype, weight, V, L.ldz, D, D, wT, s) != hipSuccess)
     return FLP_HIP_ERROR;
   void* dzT = d_weight ? at(workspace, L.dzt_off) : nullptr;
   void* hT = d_weight ? at(workspace, L.ht_off) : nullptr;
@@ -197,8 +197,10 @@ flp_status flp_backward(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
       GemmArgs g;
       g.a = dz;
       g.b = wT;
-      g.lda_b = L.ldz * int64_t(xs);
-      g.ldb_b = L.ldz * int64_t(xs);
+      g.lda_b = 128;
+      g.ldb_b = 128;
+      g.a_ks = L.ldt * 128;
+      g.b_ks = D * 128;
       g.M = rows;
       g.N = D;
       g.K = L.ldz;  // dz and W^T are zero past V
@@ -211,13 +213,15 @@ flp_status flp_backward(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
     }
     if (d_weight) {
       const int64_t kpad = round_up(rows, kTokPad);  // dz^T and hidden^T are zero past rows
-      if (launch_transpose(x_dtype, h_chunk, rows, kpad, D, D, hT, L.ldt, s) != hipSuccess)
+      if (launch_transpose(x_dtype, h_chunk, rows, kpad, D, D, hT, s) != hipSuccess)
         return FLP_HIP_ERROR;
       GemmArgs g;
       g.a = dzT;
       g.b = hT;
-      g.lda_b = L.ldt * int64_t(xs);
-      g.ldb_b = L.ldt * int64_t(xs);
+      g.lda_b = 128;
+      g.ldb_b = 128;
+      g.a_ks = L.ldz * 128;
+      g.b_ks = D * 128;
       g.M = V;
       g.N = D;
       g.K = kpad;

@@ -106,6 +106,15 @@ __device__ __forceinline__ void store4<F32>(void* base, int64_t idx, const f32x4
   *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(base) + idx) = v;
 }
 
+// K-blocked layout of the backward GEMM operands (dz, dz^T, W^T, hidden^T):
+// element (r, k) of a matrix with `rows` rows sits at ((k / KB) * rows + r) * KB
+// + k % KB, KB = 128 bytes of K.  One 128-byte pipeline stage of a GEMM tile is
+// then a contiguous block of tile rows x 128 bytes.
+template <int KB>
+__device__ __forceinline__ int64_t kblk(int64_t r, int64_t k, int64_t rows) {
+  return ((k / KB) * rows + r) * KB + (k % KB);
+}
+
 __device__ __forceinline__ int64_t load_target(const void* t, int t64, int64_t i) {
   return t64 ? reinterpret_cast<const int64_t*>(t)[i] : int64_t(reinterpret_cast<const int32_t*>(t)[i]);
 }
@@ -152,11 +161,12 @@ struct DTile {
   static_assert(ROWS % 16 == 0, "tile rows must be a multiple of 16");
   int q;                // row within the instruction's 8 rows
   int c0, c1;           // logical chunk loaded by this lane for even / odd instructions
-  int64_t ld, rows_valid;
+  int64_t ld, ks, rows_valid;  // row stride, stage stride (bytes), rows that exist
   bool full;            // every row of the tile is valid: no clamping
 
-  __device__ __forceinline__ void init(int64_t ld_, int64_t rows_valid_, int lane) {
+  __device__ __forceinline__ void init(int64_t ld_, int64_t ks_, int64_t rows_valid_, int lane) {
     ld = ld_;
+    ks = ks_;
     rows_valid = rows_valid_;
     full = rows_valid_ >= ROWS;
     q = lane >> 3;
@@ -165,7 +175,7 @@ struct DTile {
   }
   __device__ __forceinline__ void issue(const char* base, int stage, bool half, u32x4* lds,
                                         int wave) const {
-    const char* sb = base + int64_t(stage) * 128;
+    const char* sb = base + int64_t(stage) * ks;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int inst = wave * kPer + j;
@@ -257,14 +267,23 @@ struct Engine {
   __device__ __forceinline__ static void run(f32x4_t (&acc)[WMB][WNB], const char* a, int64_t lda,
                                              int64_t a_rows_valid, const char* b, int64_t ldb,
                                              int64_t b_rows_valid, int64_t kbytes, u32x4* smem) {
+    run<ODD>(acc, a, lda, 128, a_rows_valid, b, ldb, 128, b_rows_valid, kbytes, smem);
+  }
+  // The same with explicit stage strides (bytes from one 128-byte K stage of a row
+  // to the next): 128 for row-major operands, rows x 128 for K-blocked ones.
+  template <bool ODD>
+  __device__ __forceinline__ static void run(f32x4_t (&acc)[WMB][WNB], const char* a, int64_t lda,
+                                             int64_t a_ks, int64_t a_rows_valid, const char* b,
+                                             int64_t ldb, int64_t b_ks, int64_t b_rows_valid,
+                                             int64_t kbytes, u32x4* smem) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave % WM, wn = wave / WM, i = lane & 15, g = lane >> 4;
     const int nsteps = int(kbytes / kStageBytes);
     const int nst = (nsteps + 1) / 2;
     DTile<BM, NW> ta;
     DTile<BN, NW> tb;
-    ta.init(lda, a_rows_valid, lane);
-    tb.init(ldb, b_rows_valid, lane);
+    ta.init(lda, a_ks, a_rows_valid, lane);
+    tb.init(ldb, b_ks, b_rows_valid, lane);
     // Chunk of the even step for this lane; the odd step's is pos ^ 4.
     const int pos = g ^ ((i >> 1) & 7);
     const int fa = (wm * RW + i) * 8 + pos;
@@ -468,9 +487,8 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs p) {
 
 // ---- dlogits: recompute the logit tile, dz = G (onehot - p) / T, d_bias partials ------------
 //
-// dz is written row-major ([token][vocab], for d_hidden = dz W) and transposed
-// ([vocab][token], for d_weight = dz^T hidden) so that both GEMMs read
-// K-contiguous operands.  The transposed copy goes through LDS in passes of
+// dz is written token-major (for d_hidden = dz W) and transposed (for d_weight =
+// dz^T hidden), both in the K-blocked layout of the GEMM operands.  The transposed copy goes through LDS in passes of
 // CPP columns so that every vocabulary row receives BM contiguous tokens.
 // LDS staging of a bf16 [256 x 256] tile of dz for coalesced stores: 256 rows of
 // 512 bytes, each padded by 16 bytes.  Used twice: once token-major (dz rows),
@@ -554,16 +572,17 @@ __global__ __launch_bounds__(128 * WM) void k_dz(DzArgs p) {
         if constexpr (kStage) {
           acc[mb][nb] = d;
         } else {
-          if (p.dz != nullptr) store4<E>(p.dz, row * p.ldz + cw + nb * 16 + 4 * g, d);
+          constexpr int KB = 128 / E::kSize;
+          const int64_t c = cw + nb * 16 + 4 * g;
+          if (p.dz != nullptr) store4<E>(p.dz, kblk<KB>(row, c, p.ldt), d);
           if (p.dzT != nullptr) {
-            const int cl = wn * kHalfCols + nb * 16 + 4 * g;  // column within the tile
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
+              const int64_t at = kblk<KB>(c + r, row, p.ldz);
               if (E::kSize == 4)
-                reinterpret_cast<float*>(p.dzT)[(col0 + cl + r) * p.ldt + row] = d[r];
+                reinterpret_cast<float*>(p.dzT)[at] = d[r];
               else
-                reinterpret_cast<uint16_t*>(p.dzT)[(col0 + cl + r) * p.ldt + row] =
-                    uint16_t(bf16_bits_rne(d[r]));
+                reinterpret_cast<uint16_t*>(p.dzT)[at] = uint16_t(bf16_bits_rne(d[r]));
             }
           }
         }
@@ -592,7 +611,8 @@ __global__ __launch_bounds__(128 * WM) void k_dz(DzArgs p) {
         const int64_t row = row0 + tl;
         const u32x4 v = *reinterpret_cast<const u32x4*>(lds + tl * kRowB + ch * 16);
         if (row < p.rows)
-          *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.dz) + row * p.ldz + col0 + ch * 8) = v;
+          *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.dz) +
+                                    kblk<64>(row, col0 + ch * 8, p.ldt)) = v;
       }
       __syncthreads();
     }
@@ -623,8 +643,8 @@ __global__ __launch_bounds__(128 * WM) void k_dz(DzArgs p) {
       for (int idx = tid; idx < kChunks; idx += NT) {
         const int cl = idx >> 5, ch = idx & 31;
         const u32x4 v = *reinterpret_cast<const u32x4*>(lds + cl * kRowB + ch * 16);
-        *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.dzT) + (col0 + cl) * p.ldt + row0 +
-                                  ch * 8) = v;
+        *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.dzT) +
+                                  kblk<64>(col0 + cl, row0 + ch * 8, p.ldz)) = v;
       }
     }
   }
@@ -655,9 +675,9 @@ __global__ __launch_bounds__(128 * WM) void k_dz(DzArgs p) {
 
 // ---- GEMMs of the backward ----------------------------------------------------------------
 //
-// C[M x N] (+)= sum_k A[m][k] B[n][k], both operands K-contiguous.
-//   d_hidden: M = tokens, N = D, K = V (padded); A = dz [tok][ldz], B = W^T [D][ldz].
-//   d_weight: M = V, N = D, K = tokens (padded); A = dz^T [V][ldt], B = hidden^T [D][ldt].
+// C[M x N] (+)= sum_k A[m][k] B[n][k], both operands in the K-blocked layout.
+//   d_hidden: M = tokens, N = D, K = V (padded); A = dz, B = W^T.
+//   d_weight: M = V, N = D, K = tokens (padded); A = dz^T, B = hidden^T.
 // LOAD: start from the fp32 accumulator p.acc; STORE: 0 = element type to p.out,
 // 1 = fp32 to p.acc.
 template <class E, int BM, int BN, int WM, int WN, bool LOAD, int STORE>
@@ -685,9 +705,9 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(GemmArgs p) {
       acc[mb][nb] = x;
     }
   }
-  Eng::template run<false>(acc, reinterpret_cast<const char*>(p.a) + m0 * p.lda_b, p.lda_b, p.M - m0,
-           reinterpret_cast<const char*>(p.b) + n0 * p.ldb_b, p.ldb_b, p.N - n0,
-           p.K * E::kSize, smem);
+  Eng::template run<false>(acc, reinterpret_cast<const char*>(p.a) + m0 * p.lda_b, p.lda_b,
+                           p.a_ks, p.M - m0, reinterpret_cast<const char*>(p.b) + n0 * p.ldb_b,
+                           p.ldb_b, p.b_ks, p.N - n0, p.K * E::kSize, smem);
 
 #pragma unroll
   for (int mb = 0; mb < WMB; ++mb) {
@@ -705,11 +725,12 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(GemmArgs p) {
 }
 
 // ---- tiled transpose ---------------------------------------------------------------------------
-// dst[c][r] = src[r][c]; entries r in [rows, rows_pad) are written as zeros.
+// dst = src^T in the K-blocked layout (dst has `cols` rows and K = rows_pad);
+// entries r in [rows, rows_pad) are written as zeros.
 template <class T>
 __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ src, int64_t rows,
                                                    int64_t rows_pad, int64_t cols, int64_t ld_src,
-                                                   T* __restrict__ dst, int64_t ld_dst) {
+                                                   T* __restrict__ dst) {
   __shared__ T tile[64][65];
   const int64_t r0 = int64_t(blockIdx.y) * 64, c0 = int64_t(blockIdx.x) * 64;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
@@ -720,7 +741,7 @@ __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ src, in
   __syncthreads();
   for (int k = ty; k < 64; k += 4) {
     const int64_t c = c0 + k, r = r0 + tx;
-    if (r < rows_pad && c < cols) dst[c * ld_dst + r] = tile[tx][k];
+    if (r < rows_pad && c < cols) dst[kblk<128 / sizeof(T)>(c, r, cols)] = tile[tx][k];
   }
 }
 
@@ -863,16 +884,16 @@ hipError_t launch_dw(flp_dtype x, const GemmArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_transpose(flp_dtype x, const void* src, int64_t rows, int64_t rows_pad, int64_t cols,
-                            int64_t ld_src, void* dst, int64_t ld_dst, hipStream_t s) {
+                            int64_t ld_src, void* dst, hipStream_t s) {
   ProfScope ps(FLP_K_TRANSPOSE, s);
   const dim3 grid(unsigned((cols + 63) / 64), unsigned((rows_pad + 63) / 64));
   if (x == FLP_BF16)
     hipLaunchKernelGGL(k_transpose<uint16_t>, grid, dim3(256), 0, s,
                        static_cast<const uint16_t*>(src), rows, rows_pad, cols, ld_src,
-                       static_cast<uint16_t*>(dst), ld_dst);
+                       static_cast<uint16_t*>(dst));
   else
     hipLaunchKernelGGL(k_transpose<float>, grid, dim3(256), 0, s, static_cast<const float*>(src),
-                       rows, rows_pad, cols, ld_src, static_cast<float*>(dst), ld_dst);
+                       rows, rows_pad, cols, ld_src, static_cast<float*>(dst));
   return hipGetLastError();
 }
 

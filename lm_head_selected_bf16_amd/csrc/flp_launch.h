@@ -36,15 +36,16 @@ struct DzArgs {
   const float* temperature;  // chunk start or null
   const float* grad_out;     // chunk start
   const float* lse;          // chunk start
-  int64_t rows, D, V, ldz, ldt;
-  void* dz;                  // [rows_alloc][ldz], or null when d_hidden is not needed
-  void* dzT;                 // [ldz][ldt] (tokens contiguous), or null when d_weight is not needed
+  int64_t rows, D, V, ldz, ldt;  // ldz: vocabulary padded; ldt: rows allocated in the chunk
+  void* dz;                  // [ldt rows][ldz] K-blocked, or null when d_hidden is not needed
+  void* dzT;                 // [ldz rows][ldt] K-blocked, or null when d_weight is not needed
   float* dbias_part;         // [rows_alloc / kDzRowTile][ldz] or null
 };
 struct GemmArgs {
   const void* a;   // M-side operand
   const void* b;   // N-side operand
-  int64_t lda_b, ldb_b;  // row strides in bytes
+  int64_t lda_b, ldb_b;  // row strides in bytes (128 in the K-blocked layout)
+  int64_t a_ks, b_ks;    // bytes from one 128-byte K stage to the next (rows x 128)
   int64_t M, N, K;
   void* out;             // output (x dtype or fp32)
   int64_t ldo;           // elements
@@ -58,10 +59,10 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_dz(flp_dtype x, const DzArgs& a, hipStream_t s);
 hipError_t launch_dx(flp_dtype x, const GemmArgs& a, hipStream_t s);
 hipError_t launch_dw(flp_dtype x, const GemmArgs& a, hipStream_t s);
-// dst[c][r] = src[r][c] for r < rows, c < cols (row strides in elements); rows
-// [rows, rows_pad) of dst's columns are zero-filled.
+// dst = src^T for src [rows][cols] (row stride ld_src elements), written K-blocked
+// with cols rows and K = rows_pad; K entries in [rows, rows_pad) are zero-filled.
 hipError_t launch_transpose(flp_dtype x, const void* src, int64_t rows, int64_t rows_pad, int64_t cols,
-                            int64_t ld_src, void* dst, int64_t ld_dst, hipStream_t s);
+                            int64_t ld_src, void* dst, hipStream_t s);
 hipError_t launch_dbias_fold(const float* part, int64_t n_parts, int64_t ldz, int64_t V,
                              float* d_bias, int init, hipStream_t s);
 const char* kernel_ids();
