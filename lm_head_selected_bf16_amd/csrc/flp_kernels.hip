@@ -606,13 +606,15 @@ __global__ __launch_bounds__(128 * WM) void k_dz(DzArgs p) {
           *reinterpret_cast<u32x2*>(lds + tl * kRowB + cl * 2) = w;
         }
       __syncthreads();
+      // Streaming stores: dz is read back only by the next GEMM, long after it
+      // has left the caches, so it should not evict the operand tiles.
       for (int idx = tid; idx < kChunks; idx += NT) {
         const int tl = idx >> 5, ch = idx & 31;
         const int64_t row = row0 + tl;
         const u32x4 v = *reinterpret_cast<const u32x4*>(lds + tl * kRowB + ch * 16);
         if (row < p.rows)
-          *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.dz) +
-                                    kblk<64>(row, col0 + ch * 8, p.ldt)) = v;
+          __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.dz) +
+                                                                  kblk<64>(row, col0 + ch * 8, p.ldt)));
       }
       __syncthreads();
     }
@@ -643,8 +645,8 @@ __global__ __launch_bounds__(128 * WM) void k_dz(DzArgs p) {
       for (int idx = tid; idx < kChunks; idx += NT) {
         const int cl = idx >> 5, ch = idx & 31;
         const u32x4 v = *reinterpret_cast<const u32x4*>(lds + cl * kRowB + ch * 16);
-        *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.dzT) +
-                                  kblk<64>(col0 + cl, row0 + ch * 8, p.ldz)) = v;
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.dzT) +
+                                                                kblk<64>(col0 + cl, row0 + ch * 8, p.ldz)));
       }
     }
   }
