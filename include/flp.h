@@ -101,6 +101,56 @@ flp_status flp_forward(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Vocabulary shards ("Fused Linear LogP" docs page, "Tensor Parallel Vocab
+ * Shards"): a rank that holds rows [vocab_start, vocab_start + V_local) of the
+ * weight computes the per-tile partials of its slice; the partials of all
+ * shards, concatenated in ascending vocabulary order, are folded by flp_merge
+ * exactly as flp_forward folds its own, so the result is bitwise that of the
+ * unsharded call.
+ *
+ * Bytes of the partial block of a shard of V_local rows: ceil(V_local / 256)
+ * slabs x N (max, sum-of-exp) float pairs, slab-major ([slab][N] float2).
+ */
+size_t flp_forward_partial_bytes(int64_t N, int64_t V_local);
+
+/*
+ * Partial forward over one vocabulary shard.
+ *
+ *   weight       [V_local, D] x_dtype: rows vocab_start .. vocab_start + V_local - 1
+ *                of the full weight.
+ *   bias         [V_local] float32 slice of the full bias, or NULL.
+ *   targets      [N] global ids (as for flp_forward).
+ *   hidden, x_dtype, t_dtype, temperature: as for flp_forward.
+ *   partial      flp_forward_partial_bytes(N, V_local) bytes, 16-byte aligned:
+ *                the shard's [slab][N] (max, sum-of-exp) pairs.
+ *   zt           [N] float32: the scaled target logit for rows whose target is
+ *                in this shard, 0.0 for every other row, so that the shards' zt
+ *                add up exactly to the full target logits.
+ *
+ * Requirements: vocab_start % 256 == 0; V_local % 256 == 0 unless the shard
+ * ends the vocabulary (vocab_start + V_local == V_total); D % 32 == 0.
+ */
+flp_status flp_forward_partial(int64_t N, int64_t D, int64_t V_local, int64_t vocab_start,
+                               int64_t V_total, flp_dtype x_dtype, const void* hidden,
+                               const void* weight, const float* bias, const void* targets,
+                               flp_dtype t_dtype, const float* temperature, void* partial,
+                               float* zt, void* stream);
+
+/*
+ * Merge of the partials of all shards of a V_total vocabulary.
+ *
+ *   partials     [ceil(V_total / 256)][N] (max, sum-of-exp) float pairs: the
+ *                shards' partial blocks concatenated in ascending vocabulary
+ *                order; 16-byte aligned.
+ *   zt           [N] float32: the sum of the shards' zt.
+ *   targets      [N] global ids of t_dtype.
+ *   out_logp     [N] float32; out_lse [N] float32 or NULL (as for flp_forward).
+ */
+flp_status flp_merge(int64_t N, int64_t V_total, const void* partials, const float* zt,
+                     const void* targets, flp_dtype t_dtype, float* out_logp, float* out_lse,
+                     void* stream);
+
+/*
  * Backward workspace in bytes.  chunk_rows = 0 asks for the minimum (row
  * chunks of 256); a positive chunk_rows asks for the size that lets the
  * backward process that many rows per chunk (rounded up to a multiple of

@@ -33,6 +33,10 @@ SIGNATURES = {
     "flp_forward_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "flp_forward": (_int, [_i64, _i64, _i64, _int, _vp, _vp, _fp, _vp, _int, _fp, _fp, _fp, _vp,
                            _sz, _vp]),
+    "flp_forward_partial_bytes": (_sz, [_i64, _i64]),
+    "flp_forward_partial": (_int, [_i64, _i64, _i64, _i64, _i64, _int, _vp, _vp, _fp, _vp, _int, _fp,
+                                   _vp, _fp, _vp]),
+    "flp_merge": (_int, [_i64, _i64, _vp, _fp, _vp, _int, _fp, _fp, _vp]),
     "flp_backward_workspace_bytes": (_sz, [_i64, _i64, _i64, _int, _int, _i64]),
     "flp_backward": (_int, [_i64, _i64, _i64, _int, _fp, _fp, _vp, _vp, _fp, _vp, _int, _fp, _vp,
                             _vp, _int, _fp, _vp, _sz, _vp]),
@@ -81,6 +85,24 @@ def status_string(status: int) -> str:
 
 def flp_forward_workspace_bytes(N: int, D: int, V: int) -> int:
     return int(load().flp_forward_workspace_bytes(N, D, V))
+
+
+def flp_forward_partial_bytes(N: int, V_local: int) -> int:
+    return int(load().flp_forward_partial_bytes(N, V_local))
+
+
+def flp_forward_partial(N, D, V_local, vocab_start, V_total, x_dtype, hidden, weight, bias, targets,
+                        t_dtype, temperature, partial, zt, stream) -> int:
+    """Raw call: every pointer argument is an int address (0 for NULL)."""
+    return int(load().flp_forward_partial(N, D, V_local, vocab_start, V_total, x_dtype, hidden,
+                                          weight, bias, targets, t_dtype, temperature, partial,
+                                          zt, stream))
+
+
+def flp_merge(N, V_total, partials, zt, targets, t_dtype, out_logp, out_lse, stream) -> int:
+    """Raw call: every pointer argument is an int address (0 for NULL)."""
+    return int(load().flp_merge(N, V_total, partials, zt, targets, t_dtype, out_logp, out_lse,
+                                stream))
 
 
 def flp_backward_workspace_bytes(N: int, D: int, V: int, x_dtype: int, dw_dtype: int,

@@ -111,6 +111,7 @@ flp_status flp_forward(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype, const
   f.N = N;
   f.D = D;
   f.V = V;
+  f.t_off = 0;
   f.part = reinterpret_cast<float2*>(at(workspace, L.part_off));
   f.zt = reinterpret_cast<float*>(at(workspace, L.zt_off));
   if (launch_forward(x_dtype, f, s) != hipSuccess) return FLP_HIP_ERROR;
@@ -125,6 +126,60 @@ flp_status flp_forward(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype, const
   m.logp = out_logp;
   m.lse = out_lse;
   if (launch_merge(m, s) != hipSuccess) return FLP_HIP_ERROR;
+  return FLP_OK;
+}
+
+size_t flp_forward_partial_bytes(int64_t N, int64_t V_local) {
+  if (N < 0 || V_local < 1) return 0;
+  return size_t(ceil_div(V_local, kVocabTile)) * size_t(N) * 8;
+}
+
+flp_status flp_forward_partial(int64_t N, int64_t D, int64_t V_local, int64_t vocab_start,
+                               int64_t V_total, flp_dtype x_dtype, const void* hidden,
+                               const void* weight, const float* bias, const void* targets,
+                               flp_dtype t_dtype, const float* temperature, void* partial,
+                               float* zt, void* stream) {
+  flp_status st = validate_forward_partial(N, D, V_local, vocab_start, V_total, x_dtype, hidden,
+                                           weight, bias, targets, t_dtype, temperature, partial, zt);
+  if (st != FLP_OK || N == 0) return st;
+  if ((st = check_device()) != FLP_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // Rows whose target lies in another shard keep zt = 0.
+  if (launch_fill(zt, N, 0.0f, s) != hipSuccess) return FLP_HIP_ERROR;
+  FwdArgs f;
+  f.hidden = hidden;
+  f.weight = weight;
+  f.bias = bias;
+  f.targets = targets;
+  f.t64 = t_dtype == FLP_I64;
+  f.temperature = temperature;
+  f.N = N;
+  f.D = D;
+  f.V = V_local;
+  f.t_off = vocab_start;
+  f.part = static_cast<float2*>(partial);
+  f.zt = zt;
+  if (launch_forward(x_dtype, f, s) != hipSuccess) return FLP_HIP_ERROR;
+  return FLP_OK;
+}
+
+flp_status flp_merge(int64_t N, int64_t V_total, const void* partials, const float* zt,
+                     const void* targets, flp_dtype t_dtype, float* out_logp, float* out_lse,
+                     void* stream) {
+  flp_status st = validate_merge(N, V_total, partials, zt, targets, t_dtype, out_logp, out_lse);
+  if (st != FLP_OK || N == 0) return st;
+  if ((st = check_device()) != FLP_OK) return st;
+  MergeArgs m;
+  m.part = static_cast<const float2*>(partials);
+  m.zt = zt;
+  m.targets = targets;
+  m.t64 = t_dtype == FLP_I64;
+  m.N = N;
+  m.V = V_total;
+  m.n_vt = ceil_div(V_total, kVocabTile);
+  m.logp = out_logp;
+  m.lse = out_lse;
+  if (launch_merge(m, static_cast<hipStream_t>(stream)) != hipSuccess) return FLP_HIP_ERROR;
   return FLP_OK;
 }
 

@@ -413,7 +413,7 @@ __global__ __launch_bounds__(128 * WM) void k_fwd(FwdArgs p) {
     s += __shfl_xor(s, 32);
     if (g == 0) red[2 * BM + wn * BM + rl] = s;
     if (row < p.N) {
-      const int64_t t = load_target(p.targets, p.t64, row);
+      const int64_t t = load_target(p.targets, p.t64, row) - p.t_off;
       const int64_t rel = t - cw;
       if (t >= 0 && t < p.V && rel >= 0 && rel < kHalfCols && int((rel & 15) >> 2) == g) {
         const int tnb = int(rel >> 4), tr = int(rel & 3);
@@ -485,14 +485,18 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs p) {
   }
 }
 
+__global__ __launch_bounds__(256) void k_fill(float* dst, int64_t n, float value) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n) dst[i] = value;
+}
+
 // ---- dlogits: recompute the logit tile, dz = G (onehot - p) / T, d_bias partials ------------
 //
 // dz is written token-major (for d_hidden = dz W) and transposed (for d_weight =
-// dz^T hidden), both in the K-blocked layout of the GEMM operands.  The transposed copy goes through LDS in passes of
-// CPP columns so that every vocabulary row receives BM contiguous tokens.
-// LDS staging of a bf16 [256 x 256] tile of dz for coalesced stores: 256 rows of
-// 512 bytes, each padded by 16 bytes.  Used twice: once token-major (dz rows),
-// once column-major (dz^T rows).
+// dz^T hidden), both in the K-blocked layout of the GEMM operands.  A bf16
+// [256 x 256] tile is staged in LDS (256 rows of 512 bytes, each padded by 16
+// bytes), once token-major and once column-major, so that every store covers
+// whole lines.
 struct DzStage {
   static constexpr int kRowB = kTileCols * 2 + 16;
   static constexpr size_t kBytes = size_t(kTileCols) * kRowB;
@@ -863,6 +867,12 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
   ProfScope ps(FLP_K_MERGE, s);
   hipLaunchKernelGGL(k_merge, dim3(unsigned((a.N + kMergeRows - 1) / kMergeRows)), dim3(256), 0, s,
                      a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill(float* dst, int64_t n, float value, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fill, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, dst, n, value);
   return hipGetLastError();
 }
 

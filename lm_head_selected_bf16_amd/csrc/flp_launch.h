@@ -15,6 +15,7 @@ struct FwdArgs {
   int t64;
   const float* temperature;
   int64_t N, D, V;
+  int64_t t_off;    // vocabulary id of weight row 0 (0 unless a shard)
   float2* part;     // [n_vt][N]
   float* zt;        // [N]
 };
@@ -56,6 +57,7 @@ struct GemmArgs {
 
 hipError_t launch_forward(flp_dtype x, const FwdArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+hipError_t launch_fill(float* dst, int64_t n, float value, hipStream_t s);
 hipError_t launch_dz(flp_dtype x, const DzArgs& a, hipStream_t s);
 hipError_t launch_dx(flp_dtype x, const GemmArgs& a, hipStream_t s);
 hipError_t launch_dw(flp_dtype x, const GemmArgs& a, hipStream_t s);

@@ -148,6 +148,53 @@ flp_status validate_forward(int64_t N, int64_t D, int64_t V, flp_dtype x, const 
   return FLP_OK;
 }
 
+flp_status validate_forward_partial(int64_t N, int64_t D, int64_t V_local, int64_t vocab_start,
+                                    int64_t V_total, flp_dtype x, const void* hidden,
+                                    const void* weight, const float* bias, const void* targets,
+                                    flp_dtype t, const float* temperature, const void* partial,
+                                    const float* zt) {
+  flp_status st = check_dims(N, D, V_local, x, t);
+  if (st != FLP_OK) return st;
+  if (vocab_start < 0 || V_total < 1 || vocab_start > V_total - V_local) return FLP_INVALID_ARGUMENT;
+  // Shard boundaries on vocabulary-tile boundaries keep every tile, and so every
+  // partial, identical to the unsharded one.
+  if (vocab_start % kVocabTile != 0) return FLP_UNSUPPORTED_SHAPE;
+  if (V_local % kVocabTile != 0 && vocab_start + V_local != V_total) return FLP_UNSUPPORTED_SHAPE;
+  if (N == 0) return FLP_OK;
+  if (!hidden || !weight || !targets || !partial || !zt) return FLP_INVALID_ARGUMENT;
+  if (!aligned(hidden, 16) || !aligned(weight, 16) || !aligned(partial, 16) || !aligned(zt, 4) ||
+      !aligned(bias, 4) || !aligned(temperature, 4) || !aligned(targets, dtype_size(t)))
+    return FLP_MISALIGNED;
+  const size_t xs = dtype_size(x);
+  const Span ins[] = {span(hidden, size_t(N) * D * xs), span(weight, size_t(V_local) * D * xs),
+                      span(bias, size_t(V_local) * 4), span(targets, size_t(N) * dtype_size(t)),
+                      span(temperature, size_t(N) * 4)};
+  const Span outs[] = {span(partial, size_t(ceil_div(V_local, kVocabTile)) * size_t(N) * 8),
+                       span(zt, size_t(N) * 4)};
+  if (any_alias(outs, 2, ins, 5)) return FLP_INVALID_ARGUMENT;
+  return FLP_OK;
+}
+
+flp_status validate_merge(int64_t N, int64_t V_total, const void* partials, const float* zt,
+                          const void* targets, flp_dtype t, const float* out_logp,
+                          const float* out_lse) {
+  if (N < 0 || V_total < 1) return FLP_INVALID_ARGUMENT;
+  if (t != FLP_I64 && t != FLP_I32) return FLP_UNSUPPORTED_DTYPE;
+  const int64_t n_vt = ceil_div(V_total, kVocabTile);
+  if (!mul_ok(n_vt, std::max<int64_t>(N, 1)) || !mul_ok(n_vt * std::max<int64_t>(N, 1), 8))
+    return FLP_UNSUPPORTED_SHAPE;
+  if (N == 0) return FLP_OK;
+  if (!partials || !zt || !targets || !out_logp) return FLP_INVALID_ARGUMENT;
+  if (!aligned(partials, 16) || !aligned(zt, 4) || !aligned(out_logp, 4) || !aligned(out_lse, 4) ||
+      !aligned(targets, dtype_size(t)))
+    return FLP_MISALIGNED;
+  const Span ins[] = {span(partials, size_t(n_vt) * size_t(N) * 8), span(zt, size_t(N) * 4),
+                      span(targets, size_t(N) * dtype_size(t))};
+  const Span outs[] = {span(out_logp, size_t(N) * 4), span(out_lse, size_t(N) * 4)};
+  if (any_alias(outs, 2, ins, 3)) return FLP_INVALID_ARGUMENT;
+  return FLP_OK;
+}
+
 flp_status validate_backward(int64_t N, int64_t D, int64_t V, flp_dtype x, const float* grad_out,
                              const float* lse, const void* hidden, const void* weight,
                              const float* bias, const void* targets, flp_dtype t,

@@ -66,6 +66,15 @@ flp_status validate_forward(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
                             const void* targets, flp_dtype t_dtype, const float* temperature,
                             const float* out_logp, const float* out_lse,
                             const void* workspace, size_t workspace_bytes);
+// Vocabulary-shard forward and the merge of the shards' partials.
+flp_status validate_forward_partial(int64_t N, int64_t D, int64_t V_local, int64_t vocab_start,
+                                    int64_t V_total, flp_dtype x_dtype, const void* hidden,
+                                    const void* weight, const float* bias, const void* targets,
+                                    flp_dtype t_dtype, const float* temperature,
+                                    const void* partial, const float* zt);
+flp_status validate_merge(int64_t N, int64_t V_total, const void* partials, const float* zt,
+                          const void* targets, flp_dtype t_dtype, const float* out_logp,
+                          const float* out_lse);
 flp_status validate_backward(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
                              const float* grad_out, const float* lse,
                              const void* hidden, const void* weight, const float* bias,

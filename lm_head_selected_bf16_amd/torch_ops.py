@@ -93,6 +93,52 @@ def forward(hidden: torch.Tensor, weight: torch.Tensor, targets: torch.Tensor,
     return logp, lse
 
 
+def forward_partial(hidden: torch.Tensor, weight_shard: torch.Tensor, targets: torch.Tensor,
+                    vocab_start: int, vocab_size: int, bias_shard: Optional[torch.Tensor] = None,
+                    temperature: Optional[torch.Tensor] = None
+                    ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Per-tile (max, sum-of-exp) partials [ceil(V_local / 256), N, 2] and the zt [N] of one
+    vocabulary shard (rows vocab_start .. vocab_start + V_local - 1 of the weight), through
+    flp_forward_partial.  Targets are global ids; vocab_size is the full vocabulary."""
+    h2, t1, temp1, lead, N, D, V_local = _prepare(hidden, weight_shard, targets, bias_shard,
+                                                  temperature)
+    dev = hidden.device
+    partial = torch.empty(((V_local + 255) // 256, N, 2), dtype=torch.float32, device=dev)
+    zt = torch.empty(N, dtype=torch.float32, device=dev)
+    st = _abi.flp_forward_partial(N, D, V_local, int(vocab_start), int(vocab_size),
+                                  _X_DTYPES[hidden.dtype], _ptr(h2), _ptr(weight_shard),
+                                  _ptr(bias_shard), _ptr(t1), _T_DTYPES[targets.dtype],
+                                  _ptr(temp1), _ptr(partial), _ptr(zt), _stream(dev))
+    _check("flp_forward_partial", st)
+    return partial, zt
+
+
+def merge(partials: torch.Tensor, zt: torch.Tensor, targets: torch.Tensor, vocab_size: int,
+          return_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """logp (and lse) from the shards' partials concatenated in ascending vocabulary order
+    ([ceil(vocab_size / 256), N, 2]) and the sum of their zt, through flp_merge."""
+    if targets.dtype not in _T_DTYPES:
+        raise TypeError("targets must be int64 or int32")
+    lead = tuple(targets.shape)
+    t1 = targets.reshape(-1)
+    N = int(t1.shape[0])
+    n_vt = (int(vocab_size) + 255) // 256
+    if (partials.dtype != torch.float32 or tuple(partials.shape) != (n_vt, N, 2)
+            or not partials.is_contiguous()):
+        raise ValueError(f"partials must be contiguous float32 [{n_vt}, {N}, 2]")
+    if zt.dtype != torch.float32 or tuple(zt.shape) != (N,) or not zt.is_contiguous():
+        raise ValueError("zt must be contiguous float32 [N]")
+    if not t1.is_contiguous():
+        raise ValueError("targets must be contiguous")
+    dev = partials.device
+    logp = torch.empty(lead, dtype=torch.float32, device=dev)
+    lse = torch.empty(lead, dtype=torch.float32, device=dev) if return_lse else None
+    st = _abi.flp_merge(N, int(vocab_size), _ptr(partials), _ptr(zt), _ptr(t1),
+                        _T_DTYPES[targets.dtype], _ptr(logp), _ptr(lse), _stream(dev))
+    _check("flp_merge", st)
+    return logp, lse
+
+
 def backward_workspace_bytes(N: int, D: int, V: int, x_dtype: torch.dtype,
                              dw_dtype: Optional[torch.dtype] = None, chunk_rows: int = 0) -> int:
     dw = _X_DTYPES[x_dtype if dw_dtype is None else dw_dtype]

@@ -82,6 +82,63 @@ def test_forward_gates(kw, expect):
     assert abi.STATUS_NAMES[fwd(**kw)] == expect
 
 
+def fpart(**kw):
+    a = dict(N=N, D=D, VL=512, vs=256, VT=1000, x=BF16, hidden=H, weight=W, bias=B, targets=T,
+             t=I64, temp=TMP, part=LP, zt=LS, stream=0)
+    a.update(kw)
+    return abi.flp_forward_partial(a["N"], a["D"], a["VL"], a["vs"], a["VT"], a["x"], a["hidden"],
+                                   a["weight"], a["bias"], a["targets"], a["t"], a["temp"],
+                                   a["part"], a["zt"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(vs=128), "FLP_UNSUPPORTED_SHAPE"),            # shard start off a 256-column tile
+    (dict(VL=300), "FLP_UNSUPPORTED_SHAPE"),            # ragged shard that does not end V
+    (dict(vs=768, VL=512), "FLP_INVALID_ARGUMENT"),     # runs past the vocabulary
+    (dict(vs=-256), "FLP_INVALID_ARGUMENT"),
+    (dict(VL=0), "FLP_INVALID_ARGUMENT"),
+    (dict(D=40), "FLP_UNSUPPORTED_SHAPE"),
+    (dict(x=I32), "FLP_UNSUPPORTED_DTYPE"),
+    (dict(part=0), "FLP_INVALID_ARGUMENT"),
+    (dict(zt=0), "FLP_INVALID_ARGUMENT"),
+    (dict(part=LP + 8), "FLP_MISALIGNED"),
+    (dict(zt=LS + 2), "FLP_MISALIGNED"),
+    (dict(zt=H + 32), "FLP_INVALID_ARGUMENT"),          # zt inside hidden
+    (dict(part=LS - 64), "FLP_INVALID_ARGUMENT"),       # partials run into zt
+    (dict(N=0, hidden=0, targets=0, part=0, zt=0), "FLP_OK"),
+])
+def test_forward_partial_gates(kw, expect):
+    assert abi.STATUS_NAMES[fpart(**kw)] == expect
+
+
+def mrg(**kw):
+    a = dict(N=N, VT=V, part=WS, zt=TMP, targets=T, t=I32, logp=LP, lse=LS, stream=0)
+    a.update(kw)
+    return abi.flp_merge(a["N"], a["VT"], a["part"], a["zt"], a["targets"], a["t"], a["logp"],
+                         a["lse"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(N=-1), "FLP_INVALID_ARGUMENT"),
+    (dict(VT=0), "FLP_INVALID_ARGUMENT"),
+    (dict(t=F32), "FLP_UNSUPPORTED_DTYPE"),
+    (dict(part=0), "FLP_INVALID_ARGUMENT"),
+    (dict(logp=0), "FLP_INVALID_ARGUMENT"),
+    (dict(part=WS + 8), "FLP_MISALIGNED"),
+    (dict(logp=WS + 256), "FLP_INVALID_ARGUMENT"),      # output inside the partials
+    (dict(lse=LP), "FLP_INVALID_ARGUMENT"),             # the two outputs coincide
+    (dict(N=0, part=0, zt=0, targets=0, logp=0), "FLP_OK"),
+])
+def test_merge_gates(kw, expect):
+    assert abi.STATUS_NAMES[mrg(**kw)] == expect
+
+
+def test_partial_bytes():
+    assert abi.flp_forward_partial_bytes(N, 512) == 2 * N * 8
+    assert abi.flp_forward_partial_bytes(N, 513) == 3 * N * 8
+    assert abi.flp_forward_partial_bytes(N, 0) == 0
+
+
 def bwd(**kw):
     a = dict(N=N, D=D, V=V, x=BF16, g=TMP, lse=LS, hidden=H, weight=W, bias=B, targets=T, t=I64,
              temp=0, dh=0x90000000, dw=0xA0000000, dwt=BF16, db=0xB0000000, ws=WS,
