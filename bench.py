@@ -214,6 +214,54 @@ def forward_only(name: str, steps: int, warmup: int, bound: str):
     return out
 
 
+def shard_forward(name: str, shards: int, steps: int, warmup: int, bound: str):
+    """flp_forward_partial over the first of `shards` equal vocabulary shards: the
+    kernel at one rank's shape in a vocabulary tensor-parallel head."""
+    import torch
+
+    prob = Problem(name, backward=False)
+    m, g = prob.m, prob.g
+    V_local = prob.V // shards
+    w = g["weight"][:V_local].contiguous()
+    b = None if g["bias"] is None else g["bias"][:V_local].contiguous()
+    part = torch.empty(m.flp_forward_partial_bytes(prob.N, V_local), dtype=torch.uint8,
+                       device=w.device)
+    zt = torch.empty(prob.N, dtype=torch.float32, device=w.device)
+
+    def call():
+        st = m.flp_forward_partial(prob.N, prob.D, V_local, 0, prob.V, prob.x, prob.p(g["hidden"]),
+                                   prob.p(w), prob.p(b), prob.p(g["targets"]), m.FLP_I64,
+                                   prob.p(g["temperature"]), prob.p(part), prob.p(zt), prob.stream)
+        if st != m.FLP_OK:
+            raise m.FlpError("flp_forward_partial", st)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    m.flp_profile_read()
+    m.flp_profile_enable(True)
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    m.flp_profile_enable(False)
+    tot, n = m.flp_profile_read()["forward"]
+    k_ms = tot / max(n, 1)
+    out = {"workload": name, "shards": shards, "V_local": V_local, "N": prob.N,
+           "forward_kernel_ms": round(k_ms, 4)}
+    if bound == "hbm":
+        byts = V_local * prob.D * 2 + prob.N * prob.D * 2 + prob.N * 8 + prob.N * 4
+        out.update(bound="hbm", algorithmic_bytes=byts,
+                   achieved_GBs=round(byts / (k_ms / 1e3) / 1e9, 1), peak_GBs=PEAK_HBM_GBS,
+                   frac=round(byts / (k_ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4))
+    else:
+        fl = 2.0 * prob.N * prob.D * V_local
+        out.update(bound="mfma", algorithmic_flops=fl,
+                   achieved_TFLOPs=round(fl / (k_ms / 1e3) / 1e12, 1), peak_TFLOPs=PEAK_BF16_TFLOPS,
+                   frac=round(fl / (k_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4))
+    del prob
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -304,6 +352,9 @@ def main() -> int:
         out["decode_n32_forward"] = forward_only("decode_n32", 50, 10, "hbm")
         log("forward-only: rollout_n8192")
         out["rollout_n8192_forward"] = forward_only("rollout_n8192", 10, 3, "mfma")
+        log("one vocabulary shard of 8: decode_n32, rollout_n8192")
+        out["decode_n32_shard8_forward"] = shard_forward("decode_n32", 8, 50, 10, "hbm")
+        out["rollout_n8192_shard8_forward"] = shard_forward("rollout_n8192", 8, 10, 3, "mfma")
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         cpu_prob = Problem.__new__(Problem)
