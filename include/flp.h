@@ -65,7 +65,8 @@ typedef enum flp_dtype {
   FLP_BF16 = 0,   /* bfloat16, 2 bytes */
   FLP_F32 = 1,    /* IEEE binary32 */
   FLP_I64 = 2,    /* int64 target ids */
-  FLP_I32 = 3     /* int32 target ids */
+  FLP_I32 = 3,    /* int32 target ids */
+  FLP_F16 = 4     /* IEEE binary16 */
 } flp_dtype;
 
 /*
@@ -77,7 +78,8 @@ size_t flp_forward_workspace_bytes(int64_t N, int64_t D, int64_t V);
 /*
  * Forward: out_logp[i] and (optionally) out_lse[i] for every row.
  *
- *   x_dtype      FLP_BF16 or FLP_F32: element type of hidden and weight.
+ *   x_dtype      FLP_BF16, FLP_F16 or FLP_F32: element type of hidden and weight
+ *                (the docs page's Tensor Contract lists bf16 / fp16 / fp32).
  *   hidden       [N, D] x_dtype, 16-byte aligned.
  *   weight       [V, D] x_dtype, 16-byte aligned.
  *   bias         [V] float32, or NULL for no bias.

@@ -7,7 +7,7 @@ libflp.so behind the C ABI of include/flp.h.  This package holds the build
 script, the ctypes binding (same names as the C ABI) and a thin PyTorch
 wrapper with autograd.
 """
-from ._abi import (FLP_BF16, FLP_F32, FLP_I32, FLP_I64, FLP_OK, FlpError,  # noqa: F401
+from ._abi import (FLP_BF16, FLP_F16, FLP_F32, FLP_I32, FLP_I64, FLP_OK, FlpError,  # noqa: F401
                    flp_backward, flp_backward_workspace_bytes, flp_build_info, flp_forward,
                    flp_forward_partial, flp_forward_partial_bytes, flp_forward_workspace_bytes,
                    flp_merge, flp_profile_enable, flp_profile_read, flp_status_string, load)
@@ -16,7 +16,7 @@ from .torch_ops import (LinearLogp, backward, backward_workspace_bytes,  # noqa:
                         linear_logp, linear_logp_with_lse, merge)
 
 __all__ = [
-    "FLP_BF16", "FLP_F32", "FLP_I32", "FLP_I64", "FLP_OK", "FlpError",
+    "FLP_BF16", "FLP_F16", "FLP_F32", "FLP_I32", "FLP_I64", "FLP_OK", "FlpError",
     "flp_forward", "flp_backward", "flp_forward_workspace_bytes", "flp_backward_workspace_bytes",
     "flp_forward_partial", "flp_forward_partial_bytes", "flp_merge",
     "flp_status_string", "flp_build_info", "flp_profile_enable", "flp_profile_read", "load",

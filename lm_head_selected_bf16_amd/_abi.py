@@ -13,7 +13,7 @@ import threading
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflp.so")
 
 # flp_dtype
-FLP_BF16, FLP_F32, FLP_I64, FLP_I32 = 0, 1, 2, 3
+FLP_BF16, FLP_F32, FLP_I64, FLP_I32, FLP_F16 = 0, 1, 2, 3, 4
 # flp_status
 STATUS_NAMES = {
     0: "FLP_OK",

@@ -186,7 +186,7 @@ flp_status flp_merge(int64_t N, int64_t V_total, const void* partials, const flo
 size_t flp_backward_workspace_bytes(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
                                     flp_dtype dw_dtype, int64_t chunk_rows) {
   if (N < 0 || D < 1 || V < 1 || chunk_rows < 0) return 0;
-  if (x_dtype != FLP_BF16 && x_dtype != FLP_F32) return 0;
+  if (x_dtype != FLP_BF16 && x_dtype != FLP_F16 && x_dtype != FLP_F32) return 0;
   if (N == 0) return 0;
   const int64_t chunk = chunk_rows == 0 ? kRowQuantum : chunk_rows;
   return bwd_layout_for_chunk(N, D, V, x_dtype, dw_dtype, chunk, true, true, true).total;

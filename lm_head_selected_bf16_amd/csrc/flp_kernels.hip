@@ -45,6 +45,7 @@ namespace flp {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -56,6 +57,9 @@ constexpr int kTileCols = 256;    // vocabulary tile of the logits kernels
 constexpr int kHalfCols = 128;    // columns per wave column in the logits kernels
 
 struct BF16 {
+  static constexpr int kSize = 2;
+};
+struct F16 {
   static constexpr int kSize = 2;
 };
 struct F32 {
@@ -76,6 +80,12 @@ __device__ __forceinline__ void mma64<BF16>(f32x4_t& c, const u32x4& a, const u3
 }
 
 template <>
+__device__ __forceinline__ void mma64<F16>(f32x4_t& c, const u32x4& a, const u32x4& b) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                              __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+template <>
 __device__ __forceinline__ void mma64<F32>(f32x4_t& c, const u32x4& a, const u32x4& b) {
   c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
   c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
@@ -89,15 +99,29 @@ __device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
   return u >> 16;
 }
 
+// Bits of a 16-bit element type, rounded to nearest even.
+template <class E>
+__device__ __forceinline__ uint32_t bits16(float f);
+template <>
+__device__ __forceinline__ uint32_t bits16<BF16>(float f) {
+  return bf16_bits_rne(f);
+}
+template <>
+__device__ __forceinline__ uint32_t bits16<F16>(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+}
+template <class E>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  return bits16<E>(lo) | (bits16<E>(hi) << 16);
+}
+
 // Store four consecutive fp32 values as the element type.
 template <class E>
-__device__ __forceinline__ void store4(void* base, int64_t idx, const f32x4_t& v);
-
-template <>
-__device__ __forceinline__ void store4<BF16>(void* base, int64_t idx, const f32x4_t& v) {
+__device__ __forceinline__ void store4(void* base, int64_t idx, const f32x4_t& v) {
+  static_assert(E::kSize == 2, "16-bit element types");
   u32x2 w;
-  w.x = bf16_bits_rne(v.x) | (bf16_bits_rne(v.y) << 16);
-  w.y = bf16_bits_rne(v.z) | (bf16_bits_rne(v.w) << 16);
+  w.x = pack2<E>(v.x, v.y);
+  w.y = pack2<E>(v.z, v.w);
   *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(base) + idx) = w;
 }
 
@@ -512,7 +536,7 @@ template <class E, int BM, int WM, bool ODD>
 __global__ __launch_bounds__(128 * WM) void k_dz(DzArgs p) {
   using Eng = LogitEngine<E, BM, WM>;
   constexpr int RW = Eng::RW, WMB = Eng::WMB, WNB = Eng::WNB, NT = Eng::NT;
-  constexpr bool kStage = E::kSize == 2 && BM == kTileCols;  // bf16: coalesce through LDS
+  constexpr bool kStage = E::kSize == 2 && BM == kTileCols;  // 16-bit: coalesce through LDS
   extern __shared__ u32x4 smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % WM, wn = wave / WM, i = lane & 15, g = lane >> 4;
@@ -586,7 +610,7 @@ __global__ __launch_bounds__(128 * WM) void k_dz(DzArgs p) {
               if (E::kSize == 4)
                 reinterpret_cast<float*>(p.dzT)[at] = d[r];
               else
-                reinterpret_cast<uint16_t*>(p.dzT)[at] = uint16_t(bf16_bits_rne(d[r]));
+                reinterpret_cast<uint16_t*>(p.dzT)[at] = uint16_t(bits16<E>(d[r]));
             }
           }
         }
@@ -605,8 +629,8 @@ __global__ __launch_bounds__(128 * WM) void k_dz(DzArgs p) {
           const int tl = wm * RW + mb * 16 + i;
           const int cl = wn * kHalfCols + nb * 16 + 4 * g;
           u32x2 w;
-          w.x = bf16_bits_rne(acc[mb][nb][0]) | (bf16_bits_rne(acc[mb][nb][1]) << 16);
-          w.y = bf16_bits_rne(acc[mb][nb][2]) | (bf16_bits_rne(acc[mb][nb][3]) << 16);
+          w.x = pack2<E>(acc[mb][nb][0], acc[mb][nb][1]);
+          w.y = pack2<E>(acc[mb][nb][2], acc[mb][nb][3]);
           *reinterpret_cast<u32x2*>(lds + tl * kRowB + cl * 2) = w;
         }
       __syncthreads();
@@ -640,10 +664,8 @@ __global__ __launch_bounds__(128 * WM) void k_dz(DzArgs p) {
           const int c = wn * kHalfCols + nb * 16 + 4 * g + (even ? 0 : 2);
           const float lo0 = even ? d[0] : y0, hi0 = even ? y0 : d[2];
           const float lo1 = even ? d[1] : y1, hi1 = even ? y1 : d[3];
-          *reinterpret_cast<uint32_t*>(lds + c * kRowB + te * 2) =
-              bf16_bits_rne(lo0) | (bf16_bits_rne(hi0) << 16);
-          *reinterpret_cast<uint32_t*>(lds + (c + 1) * kRowB + te * 2) =
-              bf16_bits_rne(lo1) | (bf16_bits_rne(hi1) << 16);
+          *reinterpret_cast<uint32_t*>(lds + c * kRowB + te * 2) = pack2<E>(lo0, hi0);
+          *reinterpret_cast<uint32_t*>(lds + (c + 1) * kRowB + te * 2) = pack2<E>(lo1, hi1);
         }
       __syncthreads();
       for (int idx = tid; idx < kChunks; idx += NT) {
@@ -831,6 +853,10 @@ hipError_t dx_dispatch<BF16>(const GemmArgs& a, hipStream_t s) {
   return gemm_cfg<BF16, 256, 224, 4, 2, false, 0>(a, s);
 }
 template <>
+hipError_t dx_dispatch<F16>(const GemmArgs& a, hipStream_t s) {
+  return gemm_cfg<F16, 256, 224, 4, 2, false, 0>(a, s);
+}
+template <>
 hipError_t dx_dispatch<F32>(const GemmArgs& a, hipStream_t s) {
   return gemm_cfg<F32, 128, 128, 2, 2, false, 0>(a, s);
 }
@@ -847,6 +873,15 @@ hipError_t dw_dispatch<BF16>(const GemmArgs& a, hipStream_t s) {
   return gemm_cfg<BF16, 256, 224, 4, 2, false, 0>(a, s);
 }
 template <>
+hipError_t dw_dispatch<F16>(const GemmArgs& a, hipStream_t s) {
+  if (a.load_acc) {
+    if (a.store_acc) return gemm_cfg<F16, 256, 224, 4, 2, true, 1>(a, s);
+    return gemm_cfg<F16, 256, 224, 4, 2, true, 0>(a, s);
+  }
+  if (a.store_acc) return gemm_cfg<F16, 256, 224, 4, 2, false, 1>(a, s);
+  return gemm_cfg<F16, 256, 224, 4, 2, false, 0>(a, s);
+}
+template <>
 hipError_t dw_dispatch<F32>(const GemmArgs& a, hipStream_t s) {
   if (a.load_acc) {
     if (a.store_acc) return gemm_cfg<F32, 128, 128, 2, 2, true, 1>(a, s);
@@ -860,7 +895,9 @@ hipError_t dw_dispatch<F32>(const GemmArgs& a, hipStream_t s) {
 
 hipError_t launch_forward(flp_dtype x, const FwdArgs& a, hipStream_t s) {
   ProfScope ps(FLP_K_FORWARD, s);
-  return x == FLP_BF16 ? fwd_dispatch<BF16>(a, s) : fwd_dispatch<F32>(a, s);
+  if (x == FLP_BF16) return fwd_dispatch<BF16>(a, s);
+  if (x == FLP_F16) return fwd_dispatch<F16>(a, s);
+  return fwd_dispatch<F32>(a, s);
 }
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
@@ -881,25 +918,32 @@ hipError_t launch_dz(flp_dtype x, const DzArgs& a, hipStream_t s) {
   if (x == FLP_BF16)
     return odd_stages<BF16>(a.D) ? dz_cfg<BF16, int(kDzRowTile), 4, true>(a, s)
                                  : dz_cfg<BF16, int(kDzRowTile), 4, false>(a, s);
+  if (x == FLP_F16)
+    return odd_stages<F16>(a.D) ? dz_cfg<F16, int(kDzRowTile), 4, true>(a, s)
+                                : dz_cfg<F16, int(kDzRowTile), 4, false>(a, s);
   return odd_stages<F32>(a.D) ? dz_cfg<F32, int(kDzRowTile), 4, true>(a, s)
                               : dz_cfg<F32, int(kDzRowTile), 4, false>(a, s);
 }
 
 hipError_t launch_dx(flp_dtype x, const GemmArgs& a, hipStream_t s) {
   ProfScope ps(FLP_K_DHIDDEN, s);
-  return x == FLP_BF16 ? dx_dispatch<BF16>(a, s) : dx_dispatch<F32>(a, s);
+  if (x == FLP_BF16) return dx_dispatch<BF16>(a, s);
+  if (x == FLP_F16) return dx_dispatch<F16>(a, s);
+  return dx_dispatch<F32>(a, s);
 }
 
 hipError_t launch_dw(flp_dtype x, const GemmArgs& a, hipStream_t s) {
   ProfScope ps(FLP_K_DWEIGHT, s);
-  return x == FLP_BF16 ? dw_dispatch<BF16>(a, s) : dw_dispatch<F32>(a, s);
+  if (x == FLP_BF16) return dw_dispatch<BF16>(a, s);
+  if (x == FLP_F16) return dw_dispatch<F16>(a, s);
+  return dw_dispatch<F32>(a, s);
 }
 
 hipError_t launch_transpose(flp_dtype x, const void* src, int64_t rows, int64_t rows_pad, int64_t cols,
                             int64_t ld_src, void* dst, hipStream_t s) {
   ProfScope ps(FLP_K_TRANSPOSE, s);
   const dim3 grid(unsigned((cols + 63) / 64), unsigned((rows_pad + 63) / 64));
-  if (x == FLP_BF16)
+  if (x != FLP_F32)
     hipLaunchKernelGGL(k_transpose<uint16_t>, grid, dim3(256), 0, s,
                        static_cast<const uint16_t*>(src), rows, rows_pad, cols, ld_src,
                        static_cast<uint16_t*>(dst));

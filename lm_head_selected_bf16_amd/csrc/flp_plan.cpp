@@ -48,7 +48,7 @@ bool any_alias(const Span* outs, int n_out, const Span* ins, int n_in) {
 
 flp_status check_dims(int64_t N, int64_t D, int64_t V, flp_dtype x, flp_dtype t) {
   if (N < 0 || D < 1 || V < 1) return FLP_INVALID_ARGUMENT;
-  if (x != FLP_BF16 && x != FLP_F32) return FLP_UNSUPPORTED_DTYPE;
+  if (x != FLP_BF16 && x != FLP_F16 && x != FLP_F32) return FLP_UNSUPPORTED_DTYPE;
   if (t != FLP_I64 && t != FLP_I32) return FLP_UNSUPPORTED_DTYPE;
   if (D % 32 != 0) return FLP_UNSUPPORTED_SHAPE;
   const int64_t rows = std::max<int64_t>(round_up(std::max<int64_t>(N, 1), kRowQuantum), 1);

@@ -30,6 +30,7 @@ inline size_t align_up(size_t a) { return (a + kAlign - 1) / kAlign * kAlign; }
 inline size_t dtype_size(flp_dtype t) {
   switch (t) {
     case FLP_BF16: return 2;
+    case FLP_F16: return 2;
     case FLP_F32: return 4;
     case FLP_I64: return 8;
     case FLP_I32: return 4;

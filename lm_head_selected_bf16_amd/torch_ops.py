@@ -7,7 +7,8 @@ the operator.
 
 Semantics ("Fused Linear LogP" docs page, sections "Entry Point" and "Tensor
 Contract"): hidden [B, S, D] or [N, D], weight [V, D], targets [B, S] or [N]
-(int64 or int32), optional float32 bias [V]; output float32 with the leading
+(int64 or int32), optional float32 bias [V]; hidden and weight bfloat16, float16 or
+float32; output float32 with the leading
 shape of targets.  The optional per-row temperature [B, S] / [N] divides the
 logits of its row (PR #555 summary).  Gradients flow to hidden, weight and bias;
 targets and temperature are not differentiable.
@@ -19,13 +20,13 @@ from typing import Optional, Tuple
 import torch
 
 from . import _abi
-from ._abi import FLP_BF16, FLP_F32, FLP_I32, FLP_I64, FLP_OK, FlpError
+from ._abi import FLP_BF16, FLP_F16, FLP_F32, FLP_I32, FLP_I64, FLP_OK, FlpError
 
 # Default cap on the backward workspace: a larger workspace only means larger row
 # chunks (same bits); 16 GiB keeps a whole 16384-row chunk of dz and dz^T.
 DEFAULT_BWD_WORKSPACE = 16 << 30
 
-_X_DTYPES = {torch.bfloat16: FLP_BF16, torch.float32: FLP_F32}
+_X_DTYPES = {torch.bfloat16: FLP_BF16, torch.float16: FLP_F16, torch.float32: FLP_F32}
 _T_DTYPES = {torch.int64: FLP_I64, torch.int32: FLP_I32}
 
 
@@ -44,7 +45,7 @@ def _check(fn: str, status: int) -> None:
 
 def _prepare(hidden, weight, targets, bias, temperature):
     if hidden.dtype not in _X_DTYPES or weight.dtype != hidden.dtype:
-        raise TypeError("hidden and weight must both be bfloat16 or both float32")
+        raise TypeError("hidden and weight must have the same dtype: bfloat16, float16 or float32")
     if targets.dtype not in _T_DTYPES:
         raise TypeError("targets must be int64 or int32")
     if not (hidden.is_cuda and weight.is_cuda and targets.is_cuda):

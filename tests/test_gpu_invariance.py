@@ -112,3 +112,23 @@ def test_backward_chunking_is_bit_neutral(train_small):
     assert torch.equal(f1[1], f2[1])
     # bf16 d_weight is the single rounding of the fp32 one
     assert torch.equal(f1[1].to(BF16), one[1])
+
+
+def test_fp16_row_subsets():
+    """fp16 inputs take the same kernels with the fp16 MFMA: rows stay bitwise
+    independent of the batch."""
+    w = flp_inputs.Workload("fp16_inv", 300, 1000, 512, 4096, torch.float16, w_std=0.06,
+                            bias_std=0.1, n_ignored=4, ignore_values=(-1, 4096),
+                            temperature=(0.5, 1.5), grad="normal", leading=(1000,))
+    g = to_gpu(flp_inputs.make_inputs(w))
+    logp, lse = gpu_forward(g)
+    dh, _, _ = gpu_backward(g, lse, need_weight=False, need_bias=False)
+    for n in (1, 7, 257):
+        rows = flp_inputs.random_rows(1000, n, seed=300 + n).numpy()
+        sub = _subset(g, rows)
+        lp, ls = gpu_forward(sub)
+        dhs, _, _ = gpu_backward(sub, ls, need_weight=False, need_bias=False)
+        idx = torch.as_tensor(rows, device=logp.device)
+        say(f"  fp16 subset n={n}")
+        assert torch.equal(lp, logp[idx]) and torch.equal(ls, lse[idx])
+        assert torch.equal(dhs, dh[idx])

@@ -58,6 +58,9 @@ SMALL = [
     (torch.float32, 300, 96, 4133, 0.1, None, torch.int64, 5),
     (BF16, 513, 2688, 2048, 0.1, (0.5, 1.5), torch.int64, 9),
     (BF16, 1, 64, 300, None, None, torch.int64, 0),
+    # fp16 inputs (the docs page's Tensor Contract: bf16 / fp16 / fp32)
+    (torch.float16, 300, 512, 4133, 0.1, (0.5, 1.5), torch.int64, 7),
+    (torch.float16, 513, 2688, 2048, 0.1, None, torch.int32, 9),
 ]
 
 
