@@ -16,7 +16,7 @@
 // One MFMA engine serves all four contractions.  Every operand is stored
 // K-contiguous (W is transposed once per backward for d_hidden; hidden per
 // chunk for d_weight) and streamed by direct global->LDS loads
-// (global_load_lds_dwordx4, no register staging, whole 128-byte lines) into two
+// (buffer_load_dwordx4 ... lds, no register staging, whole 128-byte lines) into two
 // LDS stages of 128 bytes of K per row.  Waves form a WM x WN grid; each wave
 // owns a (BM/WM) x (BN/WN) block of 16 x 16 MFMA tiles with fp32 accumulators,
 // and double-buffers its operand fragments across the two 64-byte halves of a
@@ -199,7 +199,11 @@ struct DTile {
   }
   __device__ __forceinline__ void issue(const char* base, int stage, bool half, u32x4* lds,
                                         int wave) const {
+    // A raw buffer resource based at the stage keeps the per-lane part a 32-bit
+    // offset that does not change from stage to stage.
     const char* sb = base + int64_t(stage) * ks;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)sb, (short)0, 0x7FFFFFFF, 0x00020000);
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int inst = wave * kPer + j;
@@ -209,9 +213,8 @@ struct DTile {
         int64_t r = int64_t(inst) * 8 + q;
         if (!full) r = r < rows_valid ? r : rows_valid - 1;
         const uint32_t off = uint32_t(r * ld) + uint32_t(c * 16);
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(sb + off),
-                                         (__attribute__((address_space(3))) void*)(lds + inst * 64),
-                                         16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (__attribute__((address_space(3))) void*)(lds + inst * 64), 16, int(off), 0, 0, 0);
       }
     }
   }
@@ -607,7 +610,7 @@ __global__ __launch_bounds__(128 * WM) void k_dz(DzArgs p) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const int64_t at = kblk<KB>(c + r, row, p.ldz);
-              if (E::kSize == 4)
+              if constexpr (E::kSize == 4)
                 reinterpret_cast<float*>(p.dzT)[at] = d[r];
               else
                 reinterpret_cast<uint16_t*>(p.dzT)[at] = uint16_t(bits16<E>(d[r]));
@@ -962,10 +965,11 @@ hipError_t launch_dbias_fold(const float* part, int64_t n_parts, int64_t ldz, in
 }
 
 const char* kernel_ids() {
-  return "engine: direct global->LDS (global_load_lds_dwordx4), ring of 4-5 LDS stages x 64 B of K, "
-         "mfma_f32_16x16x32_bf16 | 16x16x4f32; k_fwd<BM 32/64/128 x BN 256 2x2 waves, BM 256 4x2 waves>; "
-         "k_merge<8 rows x 32 segments>; k_dz<BM 256 x BN 256, 4x2 waves>; k_gemm dX<256x224, 4x2 waves>; "
-         "k_gemm dW<256x224, 4x2 waves>; k_transpose; k_dbias_fold";
+  return "engine: direct global->LDS (buffer_load_dwordx4 lds, whole lines), 2 LDS stages x 128 B of K, "
+         "mfma_f32_16x16x32_bf16 | 16x16x32_f16 | 16x16x4f32; k_fwd<BM 32/64/128 x BN 256 2x2 waves, "
+         "BM 256 4x2 waves>; k_merge<8 rows x 32 segments>; k_dz<BM 256 x BN 256, 4x2 waves>; "
+         "k_gemm dX, dW<256x224, 4x2 waves, K-blocked operands>; k_transpose (K-blocked); "
+         "k_dbias_fold; k_fill";
 }
 
 }  // namespace flp
