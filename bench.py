@@ -262,6 +262,54 @@ def shard_forward(name: str, shards: int, steps: int, warmup: int, bound: str):
     return out
 
 
+def logits_op(N: int, V: int, steps: int, warmup: int):
+    """The operator on materialised logits: flp_logits_forward and flp_logits_backward over
+    N x V bf16 logits (HBM-bound: the forward reads them once, the backward reads them and
+    writes d_logits)."""
+    import torch
+
+    import flp_inputs
+    import lm_head_selected_bf16_amd as m
+
+    inp = flp_inputs.make_logits_inputs("logits_bench", N, V, torch.bfloat16, 70, n_ignored=N // 64,
+                                        ignore_values=(-1, V), device="cuda:0")
+    z, t, g = inp["logits"], inp["targets"].cuda(), inp["grad_out"].cuda()
+    logp = torch.empty(N, device="cuda:0")
+    lse = torch.empty(N, device="cuda:0")
+    d = torch.empty_like(z)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def call():
+        st = m.flp_logits_forward(N, V, m.FLP_BF16, z.data_ptr(), t.data_ptr(), m.FLP_I64,
+                                  logp.data_ptr(), lse.data_ptr(), stream)
+        st2 = m.flp_logits_backward(N, V, m.FLP_BF16, g.data_ptr(), lse.data_ptr(), z.data_ptr(),
+                                    t.data_ptr(), m.FLP_I64, d.data_ptr(), stream)
+        if st != m.FLP_OK or st2 != m.FLP_OK:
+            raise m.FlpError("flp_logits_forward/backward", st or st2)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    m.flp_profile_read()
+    m.flp_profile_enable(True)
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    m.flp_profile_enable(False)
+    prof = m.flp_profile_read()
+    out = {"workload": f"logits_n{N}: given bf16 logits [{N}, {V}], fwd (logp, lse) + bwd (d_logits)"}
+    for kind, byts in (("logits_forward", N * V * 2 + N * 16),
+                       ("logits_backward", 2 * N * V * 2 + N * 16)):
+        tot, n = prof[kind]
+        k_ms = tot / max(n, 1)
+        gbs = byts / (k_ms / 1e3) / 1e9
+        out[kind] = {"kernel_ms": round(k_ms, 4), "bound": "hbm", "algorithmic_bytes": byts,
+                     "achieved_GBs": round(gbs, 1), "peak_GBs": PEAK_HBM_GBS,
+                     "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    del z, d
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -355,6 +403,9 @@ def main() -> int:
         log("one vocabulary shard of 8: decode_n32, rollout_n8192")
         out["decode_n32_shard8_forward"] = shard_forward("decode_n32", 8, 50, 10, "hbm")
         out["rollout_n8192_shard8_forward"] = shard_forward("rollout_n8192", 8, 10, 3, "mfma")
+        torch.cuda.empty_cache()
+        log("operator on materialised logits: N=8192, V=131072")
+        out["logits_op_n8192"] = logits_op(8192, 131072, 10, 3)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         cpu_prob = Problem.__new__(Problem)

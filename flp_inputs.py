@@ -137,6 +137,26 @@ def make_inputs(name_or_workload, n_rows: Optional[int] = None, weight: Optional
     return out
 
 
+def make_logits_inputs(name: str, N: int, V: int, dtype: torch.dtype, seed: int,
+                       n_ignored: int = 0, ignore_values=(-1,), logit_std: float = 1.0,
+                       grad: str = "normal", device: str = "cpu"):
+    """Inputs of the operator on materialised logits: logits ~ N(0, logit_std^2)
+    [N, V] in `dtype`, targets (with n_ignored out-of-range rows), grad_out.
+
+    The logits are drawn on `device` from a generator seeded with 1000 * seed
+    (large blocks are drawn on the GPU directly; the same seed on the same
+    device gives the same tensor); targets, picks and grad_out are drawn on the
+    CPU with seeds 1000 * seed + 3, + 4 and + 6, as for the linear workloads.
+    """
+    w = Workload(name, seed, N, 1, V, dtype, 0.0, n_ignored=n_ignored,
+                 ignore_values=tuple(ignore_values), grad=grad, leading=(N,))
+    g = torch.Generator(device=device)
+    g.manual_seed(1000 * seed)
+    z = torch.empty(N, V, dtype=torch.float32, device=device)
+    z.normal_(0.0, logit_std, generator=g)
+    return dict(workload=w, logits=z.to(dtype), targets=draw_targets(w), grad_out=draw_grad(w))
+
+
 def random_rows(n_total: int, k: int, seed: int) -> torch.Tensor:
     """A seeded sorted sample of k distinct row indices out of n_total."""
     g = torch.Generator(device="cpu")
@@ -158,5 +178,5 @@ def ceil_div(a: int, b: int) -> int:
     return -(-a // b)
 
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "random_rows", "flops_fwd",
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "make_logits_inputs", "random_rows", "flops_fwd",
            "method_flops_fwd_bwd", "ceil_div", "math"]

@@ -153,6 +153,38 @@ flp_status flp_merge(int64_t N, int64_t V_total, const void* partials, const flo
                      void* stream);
 
 /*
+ * The sibling operator on materialised logits ("Fused LogP": the docs page's
+ * intro contrasts it with the linear op; PR #234 "Summary" and "Implementation
+ * details", PR #547 "What"): the same lse, selected log-probability and dlogits
+ * definitions applied to given logits, with no projection, bias or temperature.
+ *
+ *   logits       [N, V] x_dtype (FLP_BF16, FLP_F16 or FLP_F32), row-major,
+ *                16-byte aligned; V * element size must be a multiple of 16.
+ *   targets      [N] ids of t_dtype; an id outside [0, V) gives logp = 0 and a
+ *                zero gradient row.
+ *   out_logp     [N] float32; out_lse [N] float32 or NULL.
+ *
+ * One wave per row streams the row once (online max / sum of exp per lane in
+ * chunk order, then a fixed butterfly across the wave): a row's results do not
+ * depend on the other rows.
+ */
+flp_status flp_logits_forward(int64_t N, int64_t V, flp_dtype x_dtype, const void* logits,
+                              const void* targets, flp_dtype t_dtype, float* out_logp,
+                              float* out_lse, void* stream);
+
+/*
+ *   d_logits[i, v] = G_i (onehot(t_i)_v - exp(logits[i, v] - lse_i)),
+ *   G_i = grad_out[i] for in-range targets, else 0.
+ *
+ *   grad_out     [N] float32;  lse [N] float32 from flp_logits_forward.
+ *   d_logits     [N, V] x_dtype (RNE from fp32), 16-byte aligned; must not
+ *                overlap the inputs.
+ */
+flp_status flp_logits_backward(int64_t N, int64_t V, flp_dtype x_dtype, const float* grad_out,
+                               const float* lse, const void* logits, const void* targets,
+                               flp_dtype t_dtype, void* d_logits, void* stream);
+
+/*
  * Backward workspace in bytes.  chunk_rows = 0 asks for the minimum (row
  * chunks of 256); a positive chunk_rows asks for the size that lets the
  * backward process that many rows per chunk (rounded up to a multiple of
@@ -206,11 +238,13 @@ typedef enum flp_kernel_kind {
   FLP_K_FORWARD = 0,    /* logits tile + per-tile (max, sum of exp) + target logit */
   FLP_K_MERGE = 1,      /* ascending fold of the tile partials -> lse, logp */
   FLP_K_DLOGITS = 2,    /* logits tile recompute -> dz, dz^T, d_bias partials */
-  FLP_K_TRANSPOSE = 3,  /* hidden chunk -> hidden^T */
+  FLP_K_TRANSPOSE = 3,  /* W -> W^T, hidden chunk -> hidden^T (K-blocked) */
   FLP_K_DHIDDEN = 4,    /* d_hidden = dz W */
   FLP_K_DWEIGHT = 5,    /* d_weight (+)= dz^T hidden */
   FLP_K_DBIAS = 6,      /* ascending fold of the d_bias partials */
-  FLP_K_COUNT = 7
+  FLP_K_LOGITS_FORWARD = 7,   /* flp_logits_forward */
+  FLP_K_LOGITS_BACKWARD = 8,  /* flp_logits_backward */
+  FLP_K_COUNT = 9
 } flp_kernel_kind;
 
 void flp_profile_enable(int on);

@@ -37,6 +37,8 @@ SIGNATURES = {
     "flp_forward_partial": (_int, [_i64, _i64, _i64, _i64, _i64, _int, _vp, _vp, _fp, _vp, _int, _fp,
                                    _vp, _fp, _vp]),
     "flp_merge": (_int, [_i64, _i64, _vp, _fp, _vp, _int, _fp, _fp, _vp]),
+    "flp_logits_forward": (_int, [_i64, _i64, _int, _vp, _vp, _int, _fp, _fp, _vp]),
+    "flp_logits_backward": (_int, [_i64, _i64, _int, _fp, _fp, _vp, _vp, _int, _vp, _vp]),
     "flp_backward_workspace_bytes": (_sz, [_i64, _i64, _i64, _int, _int, _i64]),
     "flp_backward": (_int, [_i64, _i64, _i64, _int, _fp, _fp, _vp, _vp, _fp, _vp, _int, _fp, _vp,
                             _vp, _int, _fp, _vp, _sz, _vp]),
@@ -105,6 +107,19 @@ def flp_merge(N, V_total, partials, zt, targets, t_dtype, out_logp, out_lse, str
                                 stream))
 
 
+def flp_logits_forward(N, V, x_dtype, logits, targets, t_dtype, out_logp, out_lse, stream) -> int:
+    """Raw call: every pointer argument is an int address (0 for NULL)."""
+    return int(load().flp_logits_forward(N, V, x_dtype, logits, targets, t_dtype, out_logp,
+                                         out_lse, stream))
+
+
+def flp_logits_backward(N, V, x_dtype, grad_out, lse, logits, targets, t_dtype, d_logits,
+                        stream) -> int:
+    """Raw call: every pointer argument is an int address (0 for NULL)."""
+    return int(load().flp_logits_backward(N, V, x_dtype, grad_out, lse, logits, targets, t_dtype,
+                                          d_logits, stream))
+
+
 def flp_backward_workspace_bytes(N: int, D: int, V: int, x_dtype: int, dw_dtype: int,
                                  chunk_rows: int = 0) -> int:
     return int(load().flp_backward_workspace_bytes(N, D, V, x_dtype, dw_dtype, chunk_rows))
@@ -126,7 +141,8 @@ def flp_backward(N, D, V, x_dtype, grad_out, lse, hidden, weight, bias, targets,
                                    workspace, workspace_bytes, stream))
 
 
-KERNEL_KINDS = ("forward", "merge", "dlogits", "transpose", "d_hidden", "d_weight", "d_bias")
+KERNEL_KINDS = ("forward", "merge", "dlogits", "transpose", "d_hidden", "d_weight", "d_bias",
+                "logits_forward", "logits_backward")
 
 
 def flp_profile_enable(on: bool) -> None:

@@ -183,6 +183,46 @@ flp_status flp_merge(int64_t N, int64_t V_total, const void* partials, const flo
   return FLP_OK;
 }
 
+flp_status flp_logits_forward(int64_t N, int64_t V, flp_dtype x_dtype, const void* logits,
+                              const void* targets, flp_dtype t_dtype, float* out_logp,
+                              float* out_lse, void* stream) {
+  flp_status st = validate_logits_forward(N, V, x_dtype, logits, targets, t_dtype, out_logp, out_lse);
+  if (st != FLP_OK || N == 0) return st;
+  if ((st = check_device()) != FLP_OK) return st;
+  LogitsArgs a{};
+  a.logits = logits;
+  a.targets = targets;
+  a.t64 = t_dtype == FLP_I64;
+  a.N = N;
+  a.V = V;
+  a.logp = out_logp;
+  a.lse_out = out_lse;
+  if (launch_logits_forward(x_dtype, a, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return FLP_HIP_ERROR;
+  return FLP_OK;
+}
+
+flp_status flp_logits_backward(int64_t N, int64_t V, flp_dtype x_dtype, const float* grad_out,
+                               const float* lse, const void* logits, const void* targets,
+                               flp_dtype t_dtype, void* d_logits, void* stream) {
+  flp_status st = validate_logits_backward(N, V, x_dtype, grad_out, lse, logits, targets, t_dtype,
+                                           d_logits);
+  if (st != FLP_OK || N == 0) return st;
+  if ((st = check_device()) != FLP_OK) return st;
+  LogitsArgs a{};
+  a.logits = logits;
+  a.targets = targets;
+  a.t64 = t_dtype == FLP_I64;
+  a.N = N;
+  a.V = V;
+  a.grad_out = grad_out;
+  a.lse = lse;
+  a.d_logits = d_logits;
+  if (launch_logits_backward(x_dtype, a, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return FLP_HIP_ERROR;
+  return FLP_OK;
+}
+
 size_t flp_backward_workspace_bytes(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
                                     flp_dtype dw_dtype, int64_t chunk_rows) {
   if (N < 0 || D < 1 || V < 1 || chunk_rows < 0) return 0;

@@ -517,6 +517,153 @@ __global__ __launch_bounds__(256) void k_fill(float* dst, int64_t n, float value
   if (i < n) dst[i] = value;
 }
 
+// ---- the operator on materialised logits ----------------------------------------------------
+//
+// One wave per row, four rows per workgroup.  Lane l owns the 16-byte chunks
+// l, l + 64, l + 128, ... of its row and keeps an online (max, sum of exp) over
+// them in chunk order; the 64 lane pairs are then combined by a xor butterfly
+// whose combine step is symmetric, so every lane ends with the same bits.  The
+// row is read once with streaming loads, four chunks per lane in flight.
+
+template <class E>
+__device__ __forceinline__ void unpack8(const u32x4& v, float (&x)[8]);
+template <>
+__device__ __forceinline__ void unpack8<BF16>(const u32x4& v, float (&x)[8]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    x[2 * k] = __uint_as_float(v[k] << 16);
+    x[2 * k + 1] = __uint_as_float(v[k] & 0xFFFF0000u);
+  }
+}
+template <>
+__device__ __forceinline__ void unpack8<F16>(const u32x4& v, float (&x)[8]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    x[2 * k] = float(__builtin_bit_cast(_Float16, uint16_t(v[k] & 0xFFFFu)));
+    x[2 * k + 1] = float(__builtin_bit_cast(_Float16, uint16_t(v[k] >> 16)));
+  }
+}
+
+template <class E>
+__device__ __forceinline__ float load_elem(const void* base, int64_t i);
+template <>
+__device__ __forceinline__ float load_elem<BF16>(const void* base, int64_t i) {
+  return __uint_as_float(uint32_t(reinterpret_cast<const uint16_t*>(base)[i]) << 16);
+}
+template <>
+__device__ __forceinline__ float load_elem<F16>(const void* base, int64_t i) {
+  return float(reinterpret_cast<const _Float16*>(base)[i]);
+}
+template <>
+__device__ __forceinline__ float load_elem<F32>(const void* base, int64_t i) {
+  return reinterpret_cast<const float*>(base)[i];
+}
+
+template <class E>
+__global__ __launch_bounds__(256) void k_logits_fwd(LogitsArgs p) {
+  constexpr int EPC = 16 / E::kSize;  // elements per 16-byte chunk
+  constexpr int kBatch = 4;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= p.N) return;
+  const int64_t nch = p.V / EPC;
+  const u32x4* src =
+      reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(p.logits) + row * p.V * E::kSize);
+  float M = -INFINITY, S = 0.f;
+  for (int64_t c0 = lane; c0 < nch; c0 += 64 * kBatch) {
+    u32x4 v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (c0 + u * 64 < nch) v[u] = __builtin_nontemporal_load(src + c0 + u * 64);
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (c0 + u * 64 >= nch) break;
+      float x[EPC];
+      if constexpr (E::kSize == 4) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x[k] = __uint_as_float(v[u][k]);
+      } else {
+        unpack8<E>(v[u], x);
+      }
+      float cm = x[0];
+#pragma unroll
+      for (int k = 1; k < EPC; ++k) cm = fmaxf(cm, x[k]);
+      const float Mn = fmaxf(M, cm);
+      float e = 0.f;
+#pragma unroll
+      for (int k = 0; k < EPC; ++k) e += fast_exp2((x[k] - Mn) * kLog2e);
+      S = S * fast_exp2((M - Mn) * kLog2e) + e;
+      M = Mn;
+    }
+  }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float Mo = __shfl_xor(M, off), So = __shfl_xor(S, off);
+    const float Mn = fmaxf(M, Mo);
+    const float a = (M == -INFINITY) ? 0.f : S * fast_exp2((M - Mn) * kLog2e);
+    const float b = (Mo == -INFINITY) ? 0.f : So * fast_exp2((Mo - Mn) * kLog2e);
+    S = a + b;
+    M = Mn;
+  }
+  if (lane != 0) return;
+  const float ls = logf(S);
+  const int64_t t = load_target(p.targets, p.t64, row);
+  const bool valid = t >= 0 && t < p.V;
+  const float zt = valid ? load_elem<E>(p.logits, row * p.V + t) : 0.f;
+  p.logp[row] = valid ? (zt - M) - ls : 0.0f;
+  if (p.lse_out != nullptr) p.lse_out[row] = M + ls;
+}
+
+template <class E>
+__global__ __launch_bounds__(256) void k_logits_bwd(LogitsArgs p) {
+  constexpr int EPC = 16 / E::kSize;
+  constexpr int kBatch = 4;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= p.N) return;
+  const int64_t nch = p.V / EPC;
+  const u32x4* src =
+      reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(p.logits) + row * p.V * E::kSize);
+  u32x4* dst = reinterpret_cast<u32x4*>(reinterpret_cast<char*>(p.d_logits) + row * p.V * E::kSize);
+  const int64_t t = load_target(p.targets, p.t64, row);
+  const bool valid = t >= 0 && t < p.V;
+  const float G = valid ? p.grad_out[row] : 0.f;
+  const float L = p.lse[row];
+  for (int64_t c0 = lane; c0 < nch; c0 += 64 * kBatch) {
+    u32x4 v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (c0 + u * 64 < nch) v[u] = __builtin_nontemporal_load(src + c0 + u * 64);
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int64_t c = c0 + u * 64;
+      if (c >= nch) break;
+      float x[EPC], d[EPC];
+      if constexpr (E::kSize == 4) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x[k] = __uint_as_float(v[u][k]);
+      } else {
+        unpack8<E>(v[u], x);
+      }
+#pragma unroll
+      for (int k = 0; k < EPC; ++k) {
+        const float pr = fast_exp2((x[k] - L) * kLog2e);
+        const float oh = (c * EPC + k == t) ? 1.0f : 0.0f;
+        d[k] = valid ? G * (oh - pr) : 0.0f;
+      }
+      u32x4 w;
+      if constexpr (E::kSize == 4) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) w[k] = __float_as_uint(d[k]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) w[k] = pack2<E>(d[2 * k], d[2 * k + 1]);
+      }
+      __builtin_nontemporal_store(w, dst + c);
+    }
+  }
+}
+
 // ---- dlogits: recompute the logit tile, dz = G (onehot - p) / T, d_bias partials ------------
 //
 // dz is written token-major (for d_hidden = dz W) and transposed (for d_weight =
@@ -913,6 +1060,30 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
 hipError_t launch_fill(float* dst, int64_t n, float value, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_fill, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, dst, n, value);
+  return hipGetLastError();
+}
+
+hipError_t launch_logits_forward(flp_dtype x, const LogitsArgs& a, hipStream_t s) {
+  ProfScope ps(FLP_K_LOGITS_FORWARD, s);
+  const dim3 grid(unsigned((a.N + 3) / 4));
+  if (x == FLP_BF16)
+    hipLaunchKernelGGL(k_logits_fwd<BF16>, grid, dim3(256), 0, s, a);
+  else if (x == FLP_F16)
+    hipLaunchKernelGGL(k_logits_fwd<F16>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_logits_fwd<F32>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_logits_backward(flp_dtype x, const LogitsArgs& a, hipStream_t s) {
+  ProfScope ps(FLP_K_LOGITS_BACKWARD, s);
+  const dim3 grid(unsigned((a.N + 3) / 4));
+  if (x == FLP_BF16)
+    hipLaunchKernelGGL(k_logits_bwd<BF16>, grid, dim3(256), 0, s, a);
+  else if (x == FLP_F16)
+    hipLaunchKernelGGL(k_logits_bwd<F16>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_logits_bwd<F32>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

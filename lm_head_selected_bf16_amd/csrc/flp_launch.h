@@ -42,6 +42,17 @@ struct DzArgs {
   void* dzT;                 // [ldz rows][ldt] K-blocked, or null when d_weight is not needed
   float* dbias_part;         // [rows_alloc / kDzRowTile][ldz] or null
 };
+struct LogitsArgs {
+  const void* logits;        // [N][V]
+  const void* targets;
+  int t64;
+  int64_t N, V;
+  const float* grad_out;     // backward only
+  const float* lse;          // backward only
+  float* logp;               // forward only
+  float* lse_out;            // forward only, may be null
+  void* d_logits;            // backward only
+};
 struct GemmArgs {
   const void* a;   // M-side operand
   const void* b;   // N-side operand
@@ -58,6 +69,8 @@ struct GemmArgs {
 hipError_t launch_forward(flp_dtype x, const FwdArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_fill(float* dst, int64_t n, float value, hipStream_t s);
+hipError_t launch_logits_forward(flp_dtype x, const LogitsArgs& a, hipStream_t s);
+hipError_t launch_logits_backward(flp_dtype x, const LogitsArgs& a, hipStream_t s);
 hipError_t launch_dz(flp_dtype x, const DzArgs& a, hipStream_t s);
 hipError_t launch_dx(flp_dtype x, const GemmArgs& a, hipStream_t s);
 hipError_t launch_dw(flp_dtype x, const GemmArgs& a, hipStream_t s);

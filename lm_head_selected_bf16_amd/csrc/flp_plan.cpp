@@ -195,6 +195,55 @@ flp_status validate_merge(int64_t N, int64_t V_total, const void* partials, cons
   return FLP_OK;
 }
 
+namespace {
+
+flp_status check_logits_dims(int64_t N, int64_t V, flp_dtype x, flp_dtype t) {
+  if (N < 0 || V < 1) return FLP_INVALID_ARGUMENT;
+  if (x != FLP_BF16 && x != FLP_F16 && x != FLP_F32) return FLP_UNSUPPORTED_DTYPE;
+  if (t != FLP_I64 && t != FLP_I32) return FLP_UNSUPPORTED_DTYPE;
+  // Rows are streamed in 16-byte chunks.
+  if ((V * int64_t(dtype_size(x))) % 16 != 0) return FLP_UNSUPPORTED_SHAPE;
+  const int64_t n = std::max<int64_t>(N, 1);
+  if (!mul_ok(n, V) || !mul_ok(n * V, 8) || ceil_div(n, 4) > (int64_t(1) << 31) - 1)
+    return FLP_UNSUPPORTED_SHAPE;
+  return FLP_OK;
+}
+
+}  // namespace
+
+flp_status validate_logits_forward(int64_t N, int64_t V, flp_dtype x, const void* logits,
+                                   const void* targets, flp_dtype t, const float* out_logp,
+                                   const float* out_lse) {
+  flp_status st = check_logits_dims(N, V, x, t);
+  if (st != FLP_OK || N == 0) return st;
+  if (!logits || !targets || !out_logp) return FLP_INVALID_ARGUMENT;
+  if (!aligned(logits, 16) || !aligned(out_logp, 4) || !aligned(out_lse, 4) ||
+      !aligned(targets, dtype_size(t)))
+    return FLP_MISALIGNED;
+  const Span ins[] = {span(logits, size_t(N) * size_t(V) * dtype_size(x)),
+                      span(targets, size_t(N) * dtype_size(t))};
+  const Span outs[] = {span(out_logp, size_t(N) * 4), span(out_lse, size_t(N) * 4)};
+  if (any_alias(outs, 2, ins, 2)) return FLP_INVALID_ARGUMENT;
+  return FLP_OK;
+}
+
+flp_status validate_logits_backward(int64_t N, int64_t V, flp_dtype x, const float* grad_out,
+                                    const float* lse, const void* logits, const void* targets,
+                                    flp_dtype t, const void* d_logits) {
+  flp_status st = check_logits_dims(N, V, x, t);
+  if (st != FLP_OK || N == 0) return st;
+  if (!grad_out || !lse || !logits || !targets || !d_logits) return FLP_INVALID_ARGUMENT;
+  if (!aligned(logits, 16) || !aligned(d_logits, 16) || !aligned(grad_out, 4) ||
+      !aligned(lse, 4) || !aligned(targets, dtype_size(t)))
+    return FLP_MISALIGNED;
+  const Span ins[] = {span(grad_out, size_t(N) * 4), span(lse, size_t(N) * 4),
+                      span(logits, size_t(N) * size_t(V) * dtype_size(x)),
+                      span(targets, size_t(N) * dtype_size(t))};
+  const Span outs[] = {span(d_logits, size_t(N) * size_t(V) * dtype_size(x))};
+  if (any_alias(outs, 1, ins, 4)) return FLP_INVALID_ARGUMENT;
+  return FLP_OK;
+}
+
 flp_status validate_backward(int64_t N, int64_t D, int64_t V, flp_dtype x, const float* grad_out,
                              const float* lse, const void* hidden, const void* weight,
                              const float* bias, const void* targets, flp_dtype t,

@@ -76,6 +76,13 @@ flp_status validate_forward_partial(int64_t N, int64_t D, int64_t V_local, int64
 flp_status validate_merge(int64_t N, int64_t V_total, const void* partials, const float* zt,
                           const void* targets, flp_dtype t_dtype, const float* out_logp,
                           const float* out_lse);
+// The operator on materialised logits.
+flp_status validate_logits_forward(int64_t N, int64_t V, flp_dtype x_dtype, const void* logits,
+                                   const void* targets, flp_dtype t_dtype, const float* out_logp,
+                                   const float* out_lse);
+flp_status validate_logits_backward(int64_t N, int64_t V, flp_dtype x_dtype, const float* grad_out,
+                                    const float* lse, const void* logits, const void* targets,
+                                    flp_dtype t_dtype, const void* d_logits);
 flp_status validate_backward(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
                              const float* grad_out, const float* lse,
                              const void* hidden, const void* weight, const float* bias,

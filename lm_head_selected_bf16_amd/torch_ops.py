@@ -221,3 +221,72 @@ def linear_logp_with_lse(hidden, weight, targets, bias=None, temperature=None):
 def linear_logp(hidden, weight, targets, bias=None, temperature=None):
     """logp[..] = log_softmax((hidden @ weight^T + bias) / T)[target], 0 for out-of-range targets."""
     return linear_logp_with_lse(hidden, weight, targets, bias, temperature)[0]
+
+
+# ---- the operator on materialised logits ------------------------------------------------------
+
+def _prepare_logits(logits, targets):
+    if logits.dtype not in _X_DTYPES:
+        raise TypeError("logits must be bfloat16, float16 or float32")
+    if targets.dtype not in _T_DTYPES:
+        raise TypeError("targets must be int64 or int32")
+    if not (logits.is_cuda and targets.is_cuda):
+        raise ValueError("logits and targets must be on the GPU")
+    if not (logits.is_contiguous() and targets.is_contiguous()):
+        raise ValueError("logits and targets must be contiguous")
+    lead = tuple(targets.shape)
+    if tuple(logits.shape[:-1]) != lead:
+        raise ValueError("logits leading shape must equal the targets shape")
+    V = int(logits.shape[-1])
+    t1 = targets.reshape(-1)
+    return logits.reshape(-1, V), t1, lead, int(t1.shape[0]), V
+
+
+def logits_forward(logits: torch.Tensor, targets: torch.Tensor, return_lse: bool = True
+                   ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """logp (and lse) of given logits [.., V] through flp_logits_forward."""
+    z2, t1, lead, N, V = _prepare_logits(logits, targets)
+    dev = logits.device
+    logp = torch.empty(lead, dtype=torch.float32, device=dev)
+    lse = torch.empty(lead, dtype=torch.float32, device=dev) if return_lse else None
+    st = _abi.flp_logits_forward(N, V, _X_DTYPES[logits.dtype], _ptr(z2), _ptr(t1),
+                                 _T_DTYPES[targets.dtype], _ptr(logp), _ptr(lse), _stream(dev))
+    _check("flp_logits_forward", st)
+    return logp, lse
+
+
+def logits_backward(grad_out: torch.Tensor, lse: torch.Tensor, logits: torch.Tensor,
+                    targets: torch.Tensor) -> torch.Tensor:
+    """d logits (logits dtype) through flp_logits_backward."""
+    z2, t1, lead, N, V = _prepare_logits(logits, targets)
+    for name, x in (("grad_out", grad_out), ("lse", lse)):
+        if x.dtype != torch.float32 or tuple(x.shape) != lead or not x.is_contiguous():
+            raise ValueError(f"{name} must be contiguous float32 with the targets shape")
+    d = torch.empty_like(logits)
+    st = _abi.flp_logits_backward(N, V, _X_DTYPES[logits.dtype], _ptr(grad_out), _ptr(lse),
+                                  _ptr(z2), _ptr(t1), _T_DTYPES[targets.dtype], _ptr(d),
+                                  _stream(logits.device))
+    _check("flp_logits_backward", st)
+    return d
+
+
+class LogitsLogp(torch.autograd.Function):
+    """Autograd node of the operator on materialised logits; the forward saves lse."""
+
+    @staticmethod
+    def forward(ctx, logits, targets):
+        logp, lse = logits_forward(logits, targets, return_lse=True)
+        ctx.save_for_backward(logits, targets, lse)
+        return logp
+
+    @staticmethod
+    def backward(ctx, g_logp):
+        logits, targets, lse = ctx.saved_tensors
+        if not ctx.needs_input_grad[0]:
+            return None, None
+        return logits_backward(g_logp.contiguous().to(torch.float32), lse, logits, targets), None
+
+
+def logits_logp(logits, targets):
+    """logp[..] = log_softmax(logits)[target], 0 for out-of-range targets (differentiable)."""
+    return LogitsLogp.apply(logits, targets)

@@ -60,6 +60,8 @@ __all__ = [
     "dlogits",
     "forward",
     "backward",
+    "logits_forward",
+    "logits_backward",
 ]
 
 
@@ -200,3 +202,44 @@ def backward(hidden, weight, targets, grad_out, bias=None, temperature=None, row
         if need_bias:
             d_bias += dZ.sum(axis=0)
     return d_hidden, d_weight, d_bias
+
+
+# ---- the sibling operator on materialised logits ---------------------------------------------
+#
+# "Fused LogP" (the docs page's intro contrasts it with the linear op: it takes
+# already-materialised logits), with PR #547's and PR #234's conventions: the
+# same lse / selected log-probability / dlogits definitions applied to given
+# logits, no projection, no bias, no temperature.
+
+def logits_forward(logits_in, targets, rows=None, chunk=512):
+    """(logp, lse) of given logits [N, V], float64, exactly up-cast.
+
+    PR #234 "Summary" (fused logp over logits) with the Tensor Contract's
+    z[target] - logsumexp(z); out-of-range targets give 0.0 (PR #547 "What").
+    """
+    Z = as_f64(logits_in)
+    t = _as_i64(targets)
+    idx = np.arange(Z.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+    logp = np.zeros(idx.shape[0])
+    lse = np.zeros(idx.shape[0])
+    for s in range(0, idx.shape[0], chunk):
+        r = idx[s:s + chunk]
+        l = row_lse(Z[r])
+        lse[s:s + chunk] = l
+        logp[s:s + chunk] = select_logp(Z[r], l, t[r])
+    return logp, lse
+
+
+def logits_backward(logits_in, targets, grad_out, rows=None, chunk=512):
+    """d logits of sum_i g_i logp_i, float64 [rows, V] (PR #234 "Implementation
+    details": g * (one_hot(token) - softmax(logits))), recomputing lse."""
+    Z = as_f64(logits_in)
+    t = _as_i64(targets)
+    g = as_f64(grad_out)
+    idx = np.arange(Z.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.zeros((idx.shape[0], Z.shape[1]))
+    for s in range(0, idx.shape[0], chunk):
+        r = idx[s:s + chunk]
+        l = row_lse(Z[r])
+        out[s:s + chunk] = dlogits(Z[r], l, t[r], g[r])
+    return out

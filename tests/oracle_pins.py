@@ -277,4 +277,64 @@ def pin_golden_worked_example(o):
         assert np.max(np.abs(got - e[key])) < 1e-14, key
 
 
+# ---- the operator on materialised logits -----------------------------------------------------
+
+def pin_logits_op_library(o):
+    """Given logits: logp = scipy log_softmax(z)[t] (0 for ignored rows), lse = scipy logsumexp,
+    d logits = torch autograd of the f64 log_softmax-gather expression."""
+    r = _rng(40)
+    Z = r.standard_normal((8, 13)) * 2.0
+    t = r.integers(0, 13, 8)
+    t[[1, 6]] = [-1, 13]
+    g = r.standard_normal(8)
+    lp, ls = o.logits_forward(Z, t)
+    ok = (t >= 0) & (t < 13)
+    ref = scipy.special.log_softmax(Z, axis=1)[np.arange(8), np.where(ok, t, 0)]
+    assert np.max(np.abs(lp - np.where(ok, ref, 0.0))) < 1e-12
+    assert np.all(lp[~ok] == 0.0)
+    assert np.max(np.abs(ls - scipy.special.logsumexp(Z, axis=1))) < 1e-12
+    Zt = torch.tensor(Z, requires_grad=True)
+    tt = torch.tensor(t)
+    okt = (tt >= 0) & (tt < 13)
+    sel = torch.log_softmax(Zt, dim=1).gather(1, torch.where(okt, tt, 0)[:, None])[:, 0]
+    (torch.where(okt, sel, torch.zeros_like(sel)) * torch.tensor(g)).sum().backward()
+    dZ = o.logits_backward(Z, t, g)
+    assert np.max(np.abs(dZ - Zt.grad.numpy())) < 1e-12
+    assert np.all(dZ[~ok] == 0.0)
+
+
+def pin_logits_op_matches_identity_linear(o):
+    """The linear op with D = V, W = I, no bias and T = 1 is the logits op on h: both oracle
+    paths, each pinned separately, must agree."""
+    r = _rng(41)
+    H = r.standard_normal((5, 7))
+    t = r.integers(0, 7, 5)
+    g = r.standard_normal(5)
+    lp1, ls1 = o.forward(H, np.eye(7), t)
+    lp2, ls2 = o.logits_forward(H, t)
+    dh, _, _ = o.backward(H, np.eye(7), t, g)
+    dZ = o.logits_backward(H, t, g)
+    assert np.max(np.abs(lp1 - lp2)) < 1e-14 and np.max(np.abs(ls1 - ls2)) < 1e-14
+    assert np.max(np.abs(dh - dZ)) < 1e-14
+
+
+def pin_logits_op_finite_differences(o):
+    """Central finite differences of L = sum_i g_i logp_i with respect to each logit."""
+    r = _rng(42)
+    Z = r.standard_normal((3, 6))
+    t = np.array([2, -1, 5])
+    g = r.standard_normal(3)
+    an = o.logits_backward(Z, t, g)
+    num = np.zeros_like(Z)
+    h = 1e-6
+    for i in range(3):
+        for v in range(6):
+            Zp, Zm = Z.copy(), Z.copy()
+            Zp[i, v] += h
+            Zm[i, v] -= h
+            num[i, v] = ((o.logits_forward(Zp, t)[0] * g).sum()
+                         - (o.logits_forward(Zm, t)[0] * g).sum()) / (2 * h)
+    assert np.linalg.norm(num - an) / np.linalg.norm(an) < 1e-6
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

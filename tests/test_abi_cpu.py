@@ -195,3 +195,46 @@ def test_workspace_below_minimum_rejected():
     lo = abi.flp_backward_workspace_bytes(N, D, V, BF16, BF16, 0)
     for short in (1, 255, 4096, lo - 1):
         assert abi.STATUS_NAMES[bwd(wsb=short)] == "FLP_WORKSPACE_TOO_SMALL"
+
+
+def lfwd(**kw):
+    a = dict(N=N, V=1024, x=BF16, z=WS, targets=T, t=I64, logp=LP, lse=LS, stream=0)
+    a.update(kw)
+    return abi.flp_logits_forward(a["N"], a["V"], a["x"], a["z"], a["targets"], a["t"], a["logp"],
+                                  a["lse"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(N=-1), "FLP_INVALID_ARGUMENT"),
+    (dict(V=0), "FLP_INVALID_ARGUMENT"),
+    (dict(V=1001), "FLP_UNSUPPORTED_SHAPE"),            # rows must be whole 16-byte chunks
+    (dict(x=F32, V=1022), "FLP_UNSUPPORTED_SHAPE"),
+    (dict(x=I64), "FLP_UNSUPPORTED_DTYPE"),
+    (dict(t=BF16), "FLP_UNSUPPORTED_DTYPE"),
+    (dict(z=0), "FLP_INVALID_ARGUMENT"),
+    (dict(logp=0), "FLP_INVALID_ARGUMENT"),
+    (dict(z=WS + 8), "FLP_MISALIGNED"),
+    (dict(logp=WS + 64), "FLP_INVALID_ARGUMENT"),       # output inside the logits
+    (dict(N=0, z=0, targets=0, logp=0), "FLP_OK"),
+])
+def test_logits_forward_gates(kw, expect):
+    assert abi.STATUS_NAMES[lfwd(**kw)] == expect
+
+
+def lbwd(**kw):
+    a = dict(N=N, V=1024, x=BF16, g=TMP, lse=LS, z=WS, targets=T, t=I32, d=0x90000000, stream=0)
+    a.update(kw)
+    return abi.flp_logits_backward(a["N"], a["V"], a["x"], a["g"], a["lse"], a["z"], a["targets"],
+                                   a["t"], a["d"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(V=12), "FLP_UNSUPPORTED_SHAPE"),
+    (dict(g=0), "FLP_INVALID_ARGUMENT"),
+    (dict(d=0), "FLP_INVALID_ARGUMENT"),
+    (dict(d=0x90000008), "FLP_MISALIGNED"),
+    (dict(d=WS + 1024), "FLP_INVALID_ARGUMENT"),        # d_logits overlaps the logits
+    (dict(N=0, g=0, lse=0, z=0, targets=0, d=0), "FLP_OK"),
+])
+def test_logits_backward_gates(kw, expect):
+    assert abi.STATUS_NAMES[lbwd(**kw)] == expect
