@@ -923,6 +923,39 @@ __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ src, in
   }
 }
 
+// The same for 16-bit elements with 16-byte global accesses on both sides: a
+// 64 x 64 tile is read as 8 16-byte chunks per source row and written as 8
+// 16-byte chunks per destination row (one 128-byte K block).  Requires
+// 16-byte aligned source rows and rows_pad a multiple of 64.
+__global__ __launch_bounds__(256) void k_transpose16(const uint16_t* __restrict__ src, int64_t rows,
+                                                     int64_t rows_pad, int64_t cols, int64_t ld_src,
+                                                     uint16_t* __restrict__ dst) {
+  __shared__ uint32_t tile[64][33];  // [row][column pair], 132-byte rows
+  const int64_t r0 = int64_t(blockIdx.y) * 64, c0 = int64_t(blockIdx.x) * 64;
+  const int t = threadIdx.x, j = t & 7, q = t >> 3;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int rl = q + 32 * p;
+    const int64_t r = r0 + rl, c = c0 + 8 * j;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r < rows && c < cols) v = *reinterpret_cast<const u32x4*>(src + r * ld_src + c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tile[rl][4 * j + e] = v[e];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int cl = q + 32 * p;
+    const int64_t c = c0 + cl, r = r0 + 8 * j;
+    uint32_t h[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) h[k] = (tile[8 * j + k][cl >> 1] >> (16 * (cl & 1))) & 0xFFFFu;
+    const u32x4 w = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                     h[6] | (h[7] << 16)};
+    if (c < cols && r < rows_pad) *reinterpret_cast<u32x4*>(dst + kblk<64>(c, r, cols)) = w;
+  }
+}
+
 // ---- d_bias: ascending fold of the per-row-tile partials --------------------------------------
 __global__ __launch_bounds__(256) void k_dbias_fold(const float* part, int64_t n_parts, int64_t ldz,
                                                     int64_t V, float* d_bias, int init) {
@@ -1118,9 +1151,8 @@ hipError_t launch_transpose(flp_dtype x, const void* src, int64_t rows, int64_t 
   ProfScope ps(FLP_K_TRANSPOSE, s);
   const dim3 grid(unsigned((cols + 63) / 64), unsigned((rows_pad + 63) / 64));
   if (x != FLP_F32)
-    hipLaunchKernelGGL(k_transpose<uint16_t>, grid, dim3(256), 0, s,
-                       static_cast<const uint16_t*>(src), rows, rows_pad, cols, ld_src,
-                       static_cast<uint16_t*>(dst));
+    hipLaunchKernelGGL(k_transpose16, grid, dim3(256), 0, s, static_cast<const uint16_t*>(src),
+                       rows, rows_pad, cols, ld_src, static_cast<uint16_t*>(dst));
   else
     hipLaunchKernelGGL(k_transpose<float>, grid, dim3(256), 0, s, static_cast<const float*>(src),
                        rows, rows_pad, cols, ld_src, static_cast<float*>(dst));
