@@ -310,6 +310,65 @@ def logits_op(N: int, V: int, steps: int, warmup: int):
     return out
 
 
+def indexed_step(name: str, n_sel: int, steps: int, warmup: int):
+    """flp_forward_indexed + flp_backward_indexed selecting n_sel of the workload's rows (a
+    shuffled id list with repeats and out-of-range ids): the cost should follow the selected
+    rows, plus the row selection, gather and scatter kernels."""
+    import torch
+
+    import flp_inputs
+
+    prob = Problem(name, backward=False)
+    m, g, N, D, V = prob.m, prob.g, prob.N, prob.D, prob.V
+    ids = flp_inputs.row_ids(N, n_sel, seed=9, n_dup=n_sel // 16, invalid=(-1, N)).cuda()
+    n_ids = int(ids.numel())
+    fws = torch.empty(m.flp_forward_indexed_workspace_bytes(N, D, V, prob.x, n_ids),
+                      dtype=torch.uint8, device="cuda:0")
+    bws = torch.empty(m.flp_backward_indexed_workspace_bytes(N, D, V, prob.x, prob.x, n_ids,
+                                                             min(n_ids, N)),
+                      dtype=torch.uint8, device="cuda:0")
+    dh = torch.empty_like(g["hidden"])
+    dw = torch.empty_like(g["weight"])
+    db = torch.empty(V, device="cuda:0")
+    p = prob.p
+
+    def call():
+        st = m.flp_forward_indexed(N, D, V, prob.x, p(g["hidden"]), p(g["weight"]), p(g["bias"]),
+                                   p(g["targets"]), m.FLP_I64, p(g["temperature"]), p(ids),
+                                   m.FLP_I64, n_ids, p(prob.logp), p(prob.lse), p(fws),
+                                   fws.numel(), prob.stream)
+        st2 = m.flp_backward_indexed(N, D, V, prob.x, p(g["grad_out"]), p(prob.lse),
+                                     p(g["hidden"]), p(g["weight"]), p(g["bias"]),
+                                     p(g["targets"]), m.FLP_I64, p(g["temperature"]), p(ids),
+                                     m.FLP_I64, n_ids, p(dh), p(dw), prob.x,
+                                     p(db if g["bias"] is not None else None), p(bws),
+                                     bws.numel(), prob.stream)
+        if st != m.FLP_OK or st2 != m.FLP_OK:
+            raise m.FlpError("flp_forward_indexed / flp_backward_indexed", st or st2)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    m.flp_profile_read()
+    m.flp_profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    m.flp_profile_enable(False)
+    prof = m.flp_profile_read()
+    sel = int(torch.unique(ids[(ids >= 0) & (ids < N)]).numel())
+    out = {"workload": f"{name} with {sel} of its {N} rows selected by {n_ids} ids (repeats, "
+                       f"out-of-range ids): flp_forward_indexed + flp_backward_indexed",
+           "N": N, "selected": sel, "ids": n_ids, "ms_per_step": round(ms, 4),
+           "selected_tokens_per_s": round(sel / (ms / 1e3), 1),
+           "row_kernels_ms_per_step": round(prof["rows"][0] / steps, 4),
+           "method_TFLOPs": round(8.0 * min(n_ids, N) * D * V / (ms / 1e3) / 1e12, 1)}
+    del prob, fws, bws, dh, dw
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -406,6 +465,9 @@ def main() -> int:
         torch.cuda.empty_cache()
         log("operator on materialised logits: N=8192, V=131072")
         out["logits_op_n8192"] = logits_op(8192, 131072, 10, 3)
+        torch.cuda.empty_cache()
+        log("indexed: half of train_n16384's rows")
+        out["train_n16384_indexed_half"] = indexed_step(name, N // 2, 5, 2)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         cpu_prob = Problem.__new__(Problem)

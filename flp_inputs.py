@@ -164,6 +164,19 @@ def random_rows(n_total: int, k: int, seed: int) -> torch.Tensor:
     return torch.randperm(n_total, generator=g)[:k].sort().values
 
 
+def row_ids(n_total: int, k: int, seed: int, n_dup: int = 0, invalid: Tuple[int, ...] = (),
+            dtype: torch.dtype = torch.int64) -> torch.Tensor:
+    """A seeded, shuffled id list for the indexed variants: k distinct rows of n_total,
+    n_dup repeats of some of them and the given out-of-range values."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    base = torch.randperm(n_total, generator=g)[:k]
+    dup = base[torch.randint(0, max(k, 1), (n_dup,), generator=g)] if k > 0 and n_dup > 0 \
+        else torch.empty(0, dtype=torch.int64)
+    ids = torch.cat([base, dup, torch.tensor(invalid, dtype=torch.int64)])
+    return ids[torch.randperm(ids.numel(), generator=g)].to(dtype).contiguous()
+
+
 def flops_fwd(N: int, D: int, V: int) -> float:
     """Multiply-adds of the logits contraction, counted as 2 flops each."""
     return 2.0 * N * D * V

@@ -226,6 +226,64 @@ flp_status flp_backward(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Indexed (row-subset) variants (PR #547 "What", indexed semantics; PR #234
+ * "Implementation details": rows left out by an indexed call get exactly zero
+ * gradients).  A list of row ids selects which rows of the batch are computed:
+ *
+ *   rows         [n_rows] ids of r_dtype (FLP_I64 or FLP_I32), any order; may be
+ *                NULL when n_rows == 0.  An id listed more than once selects its
+ *                row once; an id outside [0, N) is ignored.
+ *
+ * Outputs keep the full row shape.  A selected row gets exactly the bits the
+ * dense call gives it; every other row gets logp = 0, lse = 0 and zero
+ * gradient rows.  d_weight and d_bias sum over the selected rows only.  The
+ * linear variants gather the selected rows into the workspace (ascending row
+ * order), run the dense kernels on them and scatter the results back, so their
+ * cost scales with min(n_rows, N), not N.  No host synchronisation: the number
+ * of distinct selected rows stays on the device, and the capacity min(n_rows, N)
+ * sizes the work.  Row ids must be below 2^31.
+ *
+ * Workspace sizes depend on n_rows; flp_backward_indexed_workspace_bytes's
+ * chunk_rows has the meaning it has for flp_backward_workspace_bytes, applied
+ * to the selected rows.
+ */
+size_t flp_forward_indexed_workspace_bytes(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
+                                           int64_t n_rows);
+flp_status flp_forward_indexed(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
+                               const void* hidden, const void* weight, const float* bias,
+                               const void* targets, flp_dtype t_dtype, const float* temperature,
+                               const void* rows, flp_dtype r_dtype, int64_t n_rows,
+                               float* out_logp, float* out_lse, void* workspace,
+                               size_t workspace_bytes, void* stream);
+size_t flp_backward_indexed_workspace_bytes(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
+                                            flp_dtype dw_dtype, int64_t n_rows,
+                                            int64_t chunk_rows);
+/* lse: [N] as written by flp_forward_indexed (or flp_forward) for the same
+ * inputs; only the selected rows are read. */
+flp_status flp_backward_indexed(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
+                                const float* grad_out, const float* lse, const void* hidden,
+                                const void* weight, const float* bias, const void* targets,
+                                flp_dtype t_dtype, const float* temperature, const void* rows,
+                                flp_dtype r_dtype, int64_t n_rows, void* d_hidden,
+                                void* d_weight, flp_dtype dw_dtype, float* d_bias,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* The operator on materialised logits, indexed: the workspace holds one byte
+ * per row (the selection mask). */
+size_t flp_logits_indexed_workspace_bytes(int64_t N);
+flp_status flp_logits_forward_indexed(int64_t N, int64_t V, flp_dtype x_dtype,
+                                      const void* logits, const void* targets, flp_dtype t_dtype,
+                                      const void* rows, flp_dtype r_dtype, int64_t n_rows,
+                                      float* out_logp, float* out_lse, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+flp_status flp_logits_backward_indexed(int64_t N, int64_t V, flp_dtype x_dtype,
+                                       const float* grad_out, const float* lse,
+                                       const void* logits, const void* targets,
+                                       flp_dtype t_dtype, const void* rows, flp_dtype r_dtype,
+                                       int64_t n_rows, void* d_logits, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
+/*
  * Optional per-kernel timing with HIP events, for benchmarks.  While enabled,
  * every kernel the library enqueues is bracketed by two events recorded on
  * the same stream; flp_profile_read synchronises those events and returns, per
@@ -244,7 +302,8 @@ typedef enum flp_kernel_kind {
   FLP_K_DBIAS = 6,      /* ascending fold of the d_bias partials */
   FLP_K_LOGITS_FORWARD = 7,   /* flp_logits_forward */
   FLP_K_LOGITS_BACKWARD = 8,  /* flp_logits_backward */
-  FLP_K_COUNT = 9
+  FLP_K_ROWS = 9,       /* indexed variants: row selection, gather, scatter */
+  FLP_K_COUNT = 10
 } flp_kernel_kind;
 
 void flp_profile_enable(int on);

@@ -42,6 +42,17 @@ SIGNATURES = {
     "flp_backward_workspace_bytes": (_sz, [_i64, _i64, _i64, _int, _int, _i64]),
     "flp_backward": (_int, [_i64, _i64, _i64, _int, _fp, _fp, _vp, _vp, _fp, _vp, _int, _fp, _vp,
                             _vp, _int, _fp, _vp, _sz, _vp]),
+    "flp_forward_indexed_workspace_bytes": (_sz, [_i64, _i64, _i64, _int, _i64]),
+    "flp_forward_indexed": (_int, [_i64, _i64, _i64, _int, _vp, _vp, _fp, _vp, _int, _fp, _vp, _int,
+                                   _i64, _fp, _fp, _vp, _sz, _vp]),
+    "flp_backward_indexed_workspace_bytes": (_sz, [_i64, _i64, _i64, _int, _int, _i64, _i64]),
+    "flp_backward_indexed": (_int, [_i64, _i64, _i64, _int, _fp, _fp, _vp, _vp, _fp, _vp, _int, _fp,
+                                    _vp, _int, _i64, _vp, _vp, _int, _fp, _vp, _sz, _vp]),
+    "flp_logits_indexed_workspace_bytes": (_sz, [_i64]),
+    "flp_logits_forward_indexed": (_int, [_i64, _i64, _int, _vp, _vp, _int, _vp, _int, _i64, _fp,
+                                          _fp, _vp, _sz, _vp]),
+    "flp_logits_backward_indexed": (_int, [_i64, _i64, _int, _fp, _fp, _vp, _vp, _int, _vp, _int,
+                                           _i64, _vp, _vp, _sz, _vp]),
     "flp_profile_enable": (None, [_int]),
     "flp_profile_read": (_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64), _int]),
     "flp_status_string": (ctypes.c_char_p, [_int]),
@@ -141,8 +152,58 @@ def flp_backward(N, D, V, x_dtype, grad_out, lse, hidden, weight, bias, targets,
                                    workspace, workspace_bytes, stream))
 
 
+def flp_forward_indexed_workspace_bytes(N: int, D: int, V: int, x_dtype: int, n_rows: int) -> int:
+    return int(load().flp_forward_indexed_workspace_bytes(N, D, V, x_dtype, n_rows))
+
+
+def flp_forward_indexed(N, D, V, x_dtype, hidden, weight, bias, targets, t_dtype, temperature,
+                        rows, r_dtype, n_rows, out_logp, out_lse, workspace, workspace_bytes,
+                        stream) -> int:
+    """Raw call: every pointer argument is an int address (0 for NULL)."""
+    return int(load().flp_forward_indexed(N, D, V, x_dtype, hidden, weight, bias, targets, t_dtype,
+                                          temperature, rows, r_dtype, n_rows, out_logp, out_lse,
+                                          workspace, workspace_bytes, stream))
+
+
+def flp_backward_indexed_workspace_bytes(N: int, D: int, V: int, x_dtype: int, dw_dtype: int,
+                                         n_rows: int, chunk_rows: int = 0) -> int:
+    return int(load().flp_backward_indexed_workspace_bytes(N, D, V, x_dtype, dw_dtype, n_rows,
+                                                           chunk_rows))
+
+
+def flp_backward_indexed(N, D, V, x_dtype, grad_out, lse, hidden, weight, bias, targets, t_dtype,
+                         temperature, rows, r_dtype, n_rows, d_hidden, d_weight, dw_dtype, d_bias,
+                         workspace, workspace_bytes, stream) -> int:
+    """Raw call: every pointer argument is an int address (0 for NULL)."""
+    return int(load().flp_backward_indexed(N, D, V, x_dtype, grad_out, lse, hidden, weight, bias,
+                                           targets, t_dtype, temperature, rows, r_dtype, n_rows,
+                                           d_hidden, d_weight, dw_dtype, d_bias, workspace,
+                                           workspace_bytes, stream))
+
+
+def flp_logits_indexed_workspace_bytes(N: int) -> int:
+    return int(load().flp_logits_indexed_workspace_bytes(N))
+
+
+def flp_logits_forward_indexed(N, V, x_dtype, logits, targets, t_dtype, rows, r_dtype, n_rows,
+                               out_logp, out_lse, workspace, workspace_bytes, stream) -> int:
+    """Raw call: every pointer argument is an int address (0 for NULL)."""
+    return int(load().flp_logits_forward_indexed(N, V, x_dtype, logits, targets, t_dtype, rows,
+                                                 r_dtype, n_rows, out_logp, out_lse, workspace,
+                                                 workspace_bytes, stream))
+
+
+def flp_logits_backward_indexed(N, V, x_dtype, grad_out, lse, logits, targets, t_dtype, rows,
+                                r_dtype, n_rows, d_logits, workspace, workspace_bytes,
+                                stream) -> int:
+    """Raw call: every pointer argument is an int address (0 for NULL)."""
+    return int(load().flp_logits_backward_indexed(N, V, x_dtype, grad_out, lse, logits, targets,
+                                                  t_dtype, rows, r_dtype, n_rows, d_logits,
+                                                  workspace, workspace_bytes, stream))
+
+
 KERNEL_KINDS = ("forward", "merge", "dlogits", "transpose", "d_hidden", "d_weight", "d_bias",
-                "logits_forward", "logits_backward")
+                "logits_forward", "logits_backward", "rows")
 
 
 def flp_profile_enable(on: bool) -> None:

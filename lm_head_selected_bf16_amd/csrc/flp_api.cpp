@@ -336,6 +336,186 @@ flp_status flp_backward(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
   return FLP_OK;
 }
 
+// ---- indexed (row-subset) variants ----
+
+size_t flp_forward_indexed_workspace_bytes(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
+                                           int64_t n_rows) {
+  if (N < 0 || D < 1 || V < 1 || n_rows < 0 || dtype_size(x_dtype) == 0) return 0;
+  if (N == 0) return 0;
+  const IdxLayout L = idx_layout(N, D, n_rows, x_dtype, false, false);
+  return L.dense_off + (L.sel.cap > 0 ? fwd_layout(L.sel.cap, D, V).total : 0);
+}
+
+flp_status flp_forward_indexed(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
+                               const void* hidden, const void* weight, const float* bias,
+                               const void* targets, flp_dtype t_dtype, const float* temperature,
+                               const void* rows, flp_dtype r_dtype, int64_t n_rows,
+                               float* out_logp, float* out_lse, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  flp_status st = validate_forward_indexed(N, D, V, x_dtype, hidden, weight, bias, targets, t_dtype,
+                                           temperature, rows, r_dtype, n_rows, out_logp, out_lse,
+                                           workspace, workspace_bytes);
+  if (st != FLP_OK || N == 0) return st;
+  if ((st = check_device()) != FLP_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const IdxLayout L = idx_layout(N, D, n_rows, x_dtype, false, false);
+  const int64_t cap = L.sel.cap;
+  auto* mask = reinterpret_cast<uint8_t*>(at(workspace, L.sel.mask_off));
+  auto* pos = reinterpret_cast<int32_t*>(at(workspace, L.sel.pos_off));
+  auto* sel = reinterpret_cast<int32_t*>(at(workspace, L.sel.sel_off));
+  if (launch_select(rows, r_dtype == FLP_I64, n_rows, N, mask, pos, sel, cap, s) != hipSuccess)
+    return FLP_HIP_ERROR;
+  float* logp_c = reinterpret_cast<float*>(at(workspace, L.logp_off));
+  float* lse_c = reinterpret_cast<float*>(at(workspace, L.lse_off));
+  if (cap > 0) {
+    GatherArgs g{};
+    g.sel = sel;
+    g.hidden = hidden;
+    g.row_bytes = D * int64_t(dtype_size(x_dtype));
+    g.targets = targets;
+    g.t64 = t_dtype == FLP_I64;
+    g.temperature = temperature;
+    g.h_c = at(workspace, L.h_off);
+    g.t_c = reinterpret_cast<int64_t*>(at(workspace, L.t_off));
+    g.temp_c = temperature ? reinterpret_cast<float*>(at(workspace, L.temp_off)) : nullptr;
+    if (launch_gather(g, cap, s) != hipSuccess) return FLP_HIP_ERROR;
+    st = flp_forward(cap, D, V, x_dtype, g.h_c, weight, bias, g.t_c, FLP_I64, g.temp_c, logp_c,
+                     lse_c, at(workspace, L.dense_off), workspace_bytes - L.dense_off, stream);
+    if (st != FLP_OK) return st;
+  }
+  if (launch_scatter_rows(pos, N, logp_c, lse_c, out_logp, out_lse, s) != hipSuccess)
+    return FLP_HIP_ERROR;
+  return FLP_OK;
+}
+
+size_t flp_backward_indexed_workspace_bytes(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
+                                            flp_dtype dw_dtype, int64_t n_rows,
+                                            int64_t chunk_rows) {
+  if (N < 0 || D < 1 || V < 1 || n_rows < 0 || chunk_rows < 0) return 0;
+  if (x_dtype != FLP_BF16 && x_dtype != FLP_F16 && x_dtype != FLP_F32) return 0;
+  if (N == 0) return 0;
+  const IdxLayout L = idx_layout(N, D, n_rows, x_dtype, true, true);
+  if (L.sel.cap == 0) return L.dense_off;
+  return L.dense_off + flp_backward_workspace_bytes(L.sel.cap, D, V, x_dtype, dw_dtype, chunk_rows);
+}
+
+flp_status flp_backward_indexed(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
+                                const float* grad_out, const float* lse, const void* hidden,
+                                const void* weight, const float* bias, const void* targets,
+                                flp_dtype t_dtype, const float* temperature, const void* rows,
+                                flp_dtype r_dtype, int64_t n_rows, void* d_hidden,
+                                void* d_weight, flp_dtype dw_dtype, float* d_bias,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  flp_status st = validate_backward_indexed(N, D, V, x_dtype, grad_out, lse, hidden, weight, bias,
+                                            targets, t_dtype, temperature, rows, r_dtype, n_rows,
+                                            d_hidden, d_weight, dw_dtype, d_bias, workspace,
+                                            workspace_bytes);
+  if (st != FLP_OK || N == 0) return st;
+  if (!d_hidden && !d_weight && !d_bias) return FLP_OK;
+  if ((st = check_device()) != FLP_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const IdxLayout L = idx_layout(N, D, n_rows, x_dtype, true, d_hidden != nullptr);
+  const int64_t cap = L.sel.cap;
+  const size_t row_bytes = size_t(D) * dtype_size(x_dtype);
+  auto* mask = reinterpret_cast<uint8_t*>(at(workspace, L.sel.mask_off));
+  auto* pos = reinterpret_cast<int32_t*>(at(workspace, L.sel.pos_off));
+  auto* sel = reinterpret_cast<int32_t*>(at(workspace, L.sel.sel_off));
+  if (launch_select(rows, r_dtype == FLP_I64, n_rows, N, mask, pos, sel, cap, s) != hipSuccess)
+    return FLP_HIP_ERROR;
+  void* dh_c = d_hidden ? at(workspace, L.dh_off) : nullptr;
+  if (cap > 0) {
+    GatherArgs g{};
+    g.sel = sel;
+    g.hidden = hidden;
+    g.row_bytes = int64_t(row_bytes);
+    g.targets = targets;
+    g.t64 = t_dtype == FLP_I64;
+    g.temperature = temperature;
+    g.grad_out = grad_out;
+    g.lse = lse;
+    g.h_c = at(workspace, L.h_off);
+    g.t_c = reinterpret_cast<int64_t*>(at(workspace, L.t_off));
+    g.temp_c = temperature ? reinterpret_cast<float*>(at(workspace, L.temp_off)) : nullptr;
+    g.g_c = reinterpret_cast<float*>(at(workspace, L.g_off));
+    g.lse_c = reinterpret_cast<float*>(at(workspace, L.lse_in_off));
+    if (launch_gather(g, cap, s) != hipSuccess) return FLP_HIP_ERROR;
+    st = flp_backward(cap, D, V, x_dtype, g.g_c, g.lse_c, g.h_c, weight, bias, g.t_c, FLP_I64,
+                      g.temp_c, dh_c, d_weight, dw_dtype, d_bias, at(workspace, L.dense_off),
+                      workspace_bytes - L.dense_off, stream);
+    if (st != FLP_OK) return st;
+  } else {
+    // Nothing can be selected: the sums over the selected rows are empty.
+    if (d_weight && launch_zero(d_weight, size_t(V) * D * dtype_size(dw_dtype), s) != hipSuccess)
+      return FLP_HIP_ERROR;
+    if (d_bias && launch_zero(d_bias, size_t(V) * 4, s) != hipSuccess) return FLP_HIP_ERROR;
+  }
+  if (d_hidden && launch_scatter_hidden(pos, N, dh_c, row_bytes, d_hidden, s) != hipSuccess)
+    return FLP_HIP_ERROR;
+  return FLP_OK;
+}
+
+size_t flp_logits_indexed_workspace_bytes(int64_t N) {
+  return N > 0 ? align_up(size_t(N)) : 0;
+}
+
+flp_status flp_logits_forward_indexed(int64_t N, int64_t V, flp_dtype x_dtype,
+                                      const void* logits, const void* targets, flp_dtype t_dtype,
+                                      const void* rows, flp_dtype r_dtype, int64_t n_rows,
+                                      float* out_logp, float* out_lse, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  flp_status st = validate_logits_indexed(N, V, x_dtype, false, nullptr, nullptr, logits, targets,
+                                          t_dtype, rows, r_dtype, n_rows, out_logp, out_lse,
+                                          workspace, workspace_bytes);
+  if (st != FLP_OK || N == 0) return st;
+  if ((st = check_device()) != FLP_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto* mask = static_cast<uint8_t*>(workspace);
+  if (launch_select(rows, r_dtype == FLP_I64, n_rows, N, mask, nullptr, nullptr, 0, s) !=
+      hipSuccess)
+    return FLP_HIP_ERROR;
+  LogitsArgs a{};
+  a.logits = logits;
+  a.targets = targets;
+  a.t64 = t_dtype == FLP_I64;
+  a.N = N;
+  a.V = V;
+  a.logp = out_logp;
+  a.lse_out = out_lse;
+  a.mask = mask;
+  if (launch_logits_forward(x_dtype, a, s) != hipSuccess) return FLP_HIP_ERROR;
+  return FLP_OK;
+}
+
+flp_status flp_logits_backward_indexed(int64_t N, int64_t V, flp_dtype x_dtype,
+                                       const float* grad_out, const float* lse,
+                                       const void* logits, const void* targets,
+                                       flp_dtype t_dtype, const void* rows, flp_dtype r_dtype,
+                                       int64_t n_rows, void* d_logits, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  flp_status st = validate_logits_indexed(N, V, x_dtype, true, grad_out, lse, logits, targets,
+                                          t_dtype, rows, r_dtype, n_rows, d_logits, nullptr,
+                                          workspace, workspace_bytes);
+  if (st != FLP_OK || N == 0) return st;
+  if ((st = check_device()) != FLP_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto* mask = static_cast<uint8_t*>(workspace);
+  if (launch_select(rows, r_dtype == FLP_I64, n_rows, N, mask, nullptr, nullptr, 0, s) !=
+      hipSuccess)
+    return FLP_HIP_ERROR;
+  LogitsArgs a{};
+  a.logits = logits;
+  a.targets = targets;
+  a.t64 = t_dtype == FLP_I64;
+  a.N = N;
+  a.V = V;
+  a.grad_out = grad_out;
+  a.lse = lse;
+  a.d_logits = d_logits;
+  a.mask = mask;
+  if (launch_logits_backward(x_dtype, a, s) != hipSuccess) return FLP_HIP_ERROR;
+  return FLP_OK;
+}
+
 void flp_profile_enable(int on) { g_prof_on.store(on != 0); }
 
 flp_status flp_profile_read(double* ms, int64_t* count, int n) {

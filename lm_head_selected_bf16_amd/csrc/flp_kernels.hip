@@ -566,6 +566,13 @@ __global__ __launch_bounds__(256) void k_logits_fwd(LogitsArgs p) {
   const int lane = threadIdx.x & 63;
   const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (row >= p.N) return;
+  if (p.mask != nullptr && p.mask[row] == 0) {  // a row left out by an indexed call
+    if (lane == 0) {
+      p.logp[row] = 0.0f;
+      if (p.lse_out != nullptr) p.lse_out[row] = 0.0f;
+    }
+    return;
+  }
   const int64_t nch = p.V / EPC;
   const u32x4* src =
       reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(p.logits) + row * p.V * E::kSize);
@@ -625,6 +632,11 @@ __global__ __launch_bounds__(256) void k_logits_bwd(LogitsArgs p) {
   const u32x4* src =
       reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(p.logits) + row * p.V * E::kSize);
   u32x4* dst = reinterpret_cast<u32x4*>(reinterpret_cast<char*>(p.d_logits) + row * p.V * E::kSize);
+  if (p.mask != nullptr && p.mask[row] == 0) {  // a row left out by an indexed call: zero gradient
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int64_t c = lane; c < nch; c += 64) __builtin_nontemporal_store(z, dst + c);
+    return;
+  }
   const int64_t t = load_target(p.targets, p.t64, row);
   const bool valid = t >= 0 && t < p.V;
   const float G = valid ? p.grad_out[row] : 0.f;
@@ -1172,7 +1184,8 @@ const char* kernel_ids() {
          "mfma_f32_16x16x32_bf16 | 16x16x32_f16 | 16x16x4f32; k_fwd<BM 32/64/128 x BN 256 2x2 waves, "
          "BM 256 4x2 waves>; k_merge<8 rows x 32 segments>; k_dz<BM 256 x BN 256, 4x2 waves>; "
          "k_gemm dX, dW<256x224, 4x2 waves, K-blocked operands>; k_transpose (K-blocked); "
-         "k_dbias_fold; k_fill";
+         "k_dbias_fold; k_fill; k_logits_fwd, k_logits_bwd<one wave per row>; "
+         "rows: k_mark, k_compact, k_gather, k_scatter_rows, k_scatter_hidden";
 }
 
 }  // namespace flp

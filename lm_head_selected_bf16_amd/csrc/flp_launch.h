@@ -52,6 +52,22 @@ struct LogitsArgs {
   float* logp;               // forward only
   float* lse_out;            // forward only, may be null
   void* d_logits;            // backward only
+  const uint8_t* mask;       // [N] selected rows (indexed variants) or null for all rows
+};
+struct GatherArgs {
+  const int32_t* sel;        // [cap] selected row ids, -1 for padding entries
+  const void* hidden;        // [N][D]
+  int64_t row_bytes;         // D * element size (a multiple of 16)
+  const void* targets;
+  int t64;
+  const float* temperature;  // may be null
+  const float* grad_out;     // may be null
+  const float* lse;          // may be null
+  void* h_c;                 // [cap][D]
+  int64_t* t_c;              // [cap]
+  float* temp_c;             // [cap] or null
+  float* g_c;                // [cap] or null
+  float* lse_c;              // [cap] or null
 };
 struct GemmArgs {
   const void* a;   // M-side operand
@@ -81,6 +97,18 @@ hipError_t launch_transpose(flp_dtype x, const void* src, int64_t rows, int64_t 
 hipError_t launch_dbias_fold(const float* part, int64_t n_parts, int64_t ldz, int64_t V,
                              float* d_bias, int init, hipStream_t s);
 const char* kernel_ids();
+
+// Row selection for the indexed variants (flp_rows.hip).  launch_zero clears
+// bytes / 4 words.  launch_select builds the mask; with pos != null it also
+// compacts it into pos / sel.
+hipError_t launch_zero(void* dst, size_t bytes, hipStream_t s);
+hipError_t launch_select(const void* rows, bool r64, int64_t n_rows, int64_t N, uint8_t* mask,
+                         int32_t* pos, int32_t* sel, int64_t cap, hipStream_t s);
+hipError_t launch_gather(const GatherArgs& a, int64_t cap, hipStream_t s);
+hipError_t launch_scatter_rows(const int32_t* pos, int64_t N, const float* logp_c,
+                               const float* lse_c, float* logp, float* lse, hipStream_t s);
+hipError_t launch_scatter_hidden(const int32_t* pos, int64_t N, const void* dh_c, size_t row_bytes,
+                                 void* dh, hipStream_t s);
 
 // Event brackets around each launch while profiling is enabled (flp_api.cpp).
 struct ProfScope {

@@ -113,8 +113,10 @@ BwdLayout bwd_layout_for_bytes(int64_t N, int64_t D, int64_t V, flp_dtype x, flp
                              (need_db ? (q / size_t(kDzRowTile)) * ldz * 4 : 0);
   const size_t fixed = ((need_dw && dw != FLP_F32) ? align_up(size_t(V) * size_t(D) * 4) : 0) +
                        (need_dh ? align_up(size_t(D) * ldz * xs) : 0);
+  // The layout of nq quanta takes fixed + nq * per_quantum bytes plus alignment
+  // padding, so this nq is an upper bound; step down to the first that fits.
   int64_t nq = 0;
-  if (per_quantum > 0 && bytes > fixed + 6 * kAlign) nq = int64_t((bytes - fixed - 6 * kAlign) / per_quantum);
+  if (per_quantum > 0 && bytes > fixed) nq = int64_t((bytes - fixed) / per_quantum);
   nq = std::min<int64_t>(nq, full / kRowQuantum);
   for (; nq >= 1; --nq) {
     L = bwd_layout_for_chunk(N, D, V, x, dw, nq * kRowQuantum, need_dh, need_dw, need_db);
@@ -122,6 +124,59 @@ BwdLayout bwd_layout_for_bytes(int64_t N, int64_t D, int64_t V, flp_dtype x, flp
   }
   L = BwdLayout();
   return L;
+}
+
+SelLayout sel_layout(int64_t N, int64_t n_rows) {
+  SelLayout L;
+  L.cap = std::max<int64_t>(std::min(n_rows, N), 0);
+  size_t off = 0;
+  L.mask_off = off;
+  off += align_up(size_t(std::max<int64_t>(N, 0)));
+  L.pos_off = off;
+  off += align_up(size_t(std::max<int64_t>(N, 0)) * 4);
+  L.sel_off = off;
+  off += align_up(size_t(L.cap) * 4);
+  L.total = std::max<size_t>(off, kAlign);
+  return L;
+}
+
+IdxLayout idx_layout(int64_t N, int64_t D, int64_t n_rows, flp_dtype x, bool backward,
+                     bool need_dh) {
+  IdxLayout L;
+  L.sel = sel_layout(N, n_rows);
+  const size_t c = size_t(L.sel.cap);
+  const size_t row_bytes = size_t(D) * dtype_size(x);
+  size_t off = L.sel.total;
+  L.h_off = off;
+  off += align_up(c * row_bytes);
+  L.t_off = off;
+  off += align_up(c * 8);
+  L.temp_off = off;
+  off += align_up(c * 4);
+  if (backward) {
+    L.g_off = off;
+    off += align_up(c * 4);
+    L.lse_in_off = off;
+    off += align_up(c * 4);
+    L.dh_off = off;
+    if (need_dh) off += align_up(c * row_bytes);
+  } else {
+    L.logp_off = off;
+    off += align_up(c * 4);
+    L.lse_off = off;
+    off += align_up(c * 4);
+  }
+  L.dense_off = off;
+  return L;
+}
+
+flp_status validate_rows(int64_t N, const void* rows, flp_dtype r, int64_t n_rows) {
+  if (N < 0 || n_rows < 0) return FLP_INVALID_ARGUMENT;
+  if (r != FLP_I64 && r != FLP_I32) return FLP_UNSUPPORTED_DTYPE;
+  if (N > kMaxIndexedRows || n_rows > kMaxIndex / 8) return FLP_UNSUPPORTED_SHAPE;
+  if (n_rows > 0 && rows == nullptr) return FLP_INVALID_ARGUMENT;
+  if (!aligned(rows, dtype_size(r))) return FLP_MISALIGNED;
+  return FLP_OK;
 }
 
 flp_status validate_forward(int64_t N, int64_t D, int64_t V, flp_dtype x, const void* hidden,
@@ -274,6 +329,99 @@ flp_status validate_backward(int64_t N, int64_t D, int64_t V, flp_dtype x, const
   const BwdLayout L = bwd_layout_for_bytes(N, D, V, x, dw, workspace_bytes, d_hidden != nullptr,
                                            d_weight != nullptr, d_bias != nullptr);
   if (L.chunk == 0) return FLP_WORKSPACE_TOO_SMALL;
+  return FLP_OK;
+}
+
+flp_status validate_forward_indexed(int64_t N, int64_t D, int64_t V, flp_dtype x,
+                                    const void* hidden, const void* weight, const float* bias,
+                                    const void* targets, flp_dtype t, const float* temperature,
+                                    const void* rows, flp_dtype r, int64_t n_rows,
+                                    const float* out_logp, const float* out_lse,
+                                    const void* workspace, size_t workspace_bytes) {
+  flp_status st = check_dims(N, D, V, x, t);
+  if (st != FLP_OK) return st;
+  if ((st = validate_rows(N, rows, r, n_rows)) != FLP_OK) return st;
+  if (N == 0) return FLP_OK;
+  if (!hidden || !weight || !targets || !out_logp || !workspace) return FLP_INVALID_ARGUMENT;
+  if (!aligned(hidden, 16) || !aligned(weight, 16) || !aligned(workspace, 16) ||
+      !aligned(bias, 4) || !aligned(temperature, 4) || !aligned(out_logp, 4) ||
+      !aligned(out_lse, 4) || !aligned(targets, dtype_size(t)))
+    return FLP_MISALIGNED;
+  const size_t xs = dtype_size(x);
+  const Span ins[] = {span(hidden, size_t(N) * D * xs), span(weight, size_t(V) * D * xs),
+                      span(bias, size_t(V) * 4), span(targets, size_t(N) * dtype_size(t)),
+                      span(temperature, size_t(N) * 4), span(rows, size_t(n_rows) * dtype_size(r))};
+  const Span outs[] = {span(out_logp, size_t(N) * 4), span(out_lse, size_t(N) * 4),
+                       span(workspace, workspace_bytes)};
+  if (any_alias(outs, 3, ins, 6)) return FLP_INVALID_ARGUMENT;
+  const IdxLayout L = idx_layout(N, D, n_rows, x, false, false);
+  const size_t need = L.dense_off + (L.sel.cap > 0 ? fwd_layout(L.sel.cap, D, V).total : 0);
+  if (workspace_bytes < need) return FLP_WORKSPACE_TOO_SMALL;
+  return FLP_OK;
+}
+
+flp_status validate_backward_indexed(int64_t N, int64_t D, int64_t V, flp_dtype x,
+                                     const float* grad_out, const float* lse, const void* hidden,
+                                     const void* weight, const float* bias, const void* targets,
+                                     flp_dtype t, const float* temperature, const void* rows,
+                                     flp_dtype r, int64_t n_rows, const void* d_hidden,
+                                     const void* d_weight, flp_dtype dw, const float* d_bias,
+                                     const void* workspace, size_t workspace_bytes) {
+  flp_status st = check_dims(N, D, V, x, t);
+  if (st != FLP_OK) return st;
+  if (dw != x && dw != FLP_F32) return FLP_UNSUPPORTED_DTYPE;
+  if ((st = validate_rows(N, rows, r, n_rows)) != FLP_OK) return st;
+  if (N == 0) return FLP_OK;
+  if (!grad_out || !lse || !hidden || !weight || !targets) return FLP_INVALID_ARGUMENT;
+  if (!d_hidden && !d_weight && !d_bias) return FLP_OK;
+  if (!workspace) return FLP_INVALID_ARGUMENT;
+  const size_t xs = dtype_size(x);
+  if (!aligned(hidden, 16) || !aligned(weight, 16) || !aligned(workspace, 16) ||
+      !aligned(grad_out, 4) || !aligned(lse, 4) || !aligned(bias, 4) ||
+      !aligned(temperature, 4) || !aligned(targets, dtype_size(t)) ||
+      !aligned(d_hidden, 16) || !aligned(d_weight, 16) || !aligned(d_bias, 4))
+    return FLP_MISALIGNED;
+  const Span ins[] = {span(grad_out, size_t(N) * 4), span(lse, size_t(N) * 4),
+                      span(hidden, size_t(N) * D * xs), span(weight, size_t(V) * D * xs),
+                      span(bias, size_t(V) * 4), span(targets, size_t(N) * dtype_size(t)),
+                      span(temperature, size_t(N) * 4), span(rows, size_t(n_rows) * dtype_size(r))};
+  const Span outs[] = {span(d_hidden, size_t(N) * D * xs),
+                       span(d_weight, size_t(V) * D * dtype_size(dw)),
+                       span(d_bias, size_t(V) * 4), span(workspace, workspace_bytes)};
+  if (any_alias(outs, 4, ins, 8)) return FLP_INVALID_ARGUMENT;
+  const IdxLayout L = idx_layout(N, D, n_rows, x, true, d_hidden != nullptr);
+  if (workspace_bytes < L.dense_off) return FLP_WORKSPACE_TOO_SMALL;
+  if (L.sel.cap > 0 &&
+      bwd_layout_for_bytes(L.sel.cap, D, V, x, dw, workspace_bytes - L.dense_off,
+                           d_hidden != nullptr, d_weight != nullptr, d_bias != nullptr)
+              .chunk == 0)
+    return FLP_WORKSPACE_TOO_SMALL;
+  return FLP_OK;
+}
+
+flp_status validate_logits_indexed(int64_t N, int64_t V, flp_dtype x, bool backward,
+                                   const float* grad_out, const float* lse, const void* logits,
+                                   const void* targets, flp_dtype t, const void* rows,
+                                   flp_dtype r, int64_t n_rows, const void* out_a,
+                                   const void* out_b, const void* workspace,
+                                   size_t workspace_bytes) {
+  flp_status st = check_logits_dims(N, V, x, t);
+  if (st != FLP_OK) return st;
+  if ((st = validate_rows(N, rows, r, n_rows)) != FLP_OK) return st;
+  if (N == 0) return FLP_OK;
+  if (!logits || !targets || !out_a || !workspace) return FLP_INVALID_ARGUMENT;
+  if (backward && (!grad_out || !lse)) return FLP_INVALID_ARGUMENT;
+  const size_t row_out = backward ? size_t(V) * dtype_size(x) : 4;
+  if (!aligned(logits, 16) || !aligned(out_a, backward ? 16 : 4) || !aligned(out_b, 4) ||
+      !aligned(grad_out, 4) || !aligned(lse, 4) || !aligned(targets, dtype_size(t)))
+    return FLP_MISALIGNED;
+  const Span ins[] = {span(logits, size_t(N) * size_t(V) * dtype_size(x)),
+                      span(targets, size_t(N) * dtype_size(t)), span(grad_out, size_t(N) * 4),
+                      span(lse, size_t(N) * 4), span(rows, size_t(n_rows) * dtype_size(r))};
+  const Span outs[] = {span(out_a, size_t(N) * row_out), span(out_b, size_t(N) * 4),
+                       span(workspace, workspace_bytes)};
+  if (any_alias(outs, 3, ins, 5)) return FLP_INVALID_ARGUMENT;
+  if (workspace_bytes < align_up(size_t(N))) return FLP_WORKSPACE_TOO_SMALL;
   return FLP_OK;
 }
 

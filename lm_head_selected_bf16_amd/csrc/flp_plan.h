@@ -61,6 +61,27 @@ BwdLayout bwd_layout_for_chunk(int64_t N, int64_t D, int64_t V, flp_dtype x, flp
 BwdLayout bwd_layout_for_bytes(int64_t N, int64_t D, int64_t V, flp_dtype x, flp_dtype dw,
                                size_t bytes, bool need_dh, bool need_dw, bool need_db);
 
+// ---- indexed variants: row selection and the gathered copy of the selected rows ----
+// Largest N the indexed variants take (compact positions are int32).
+constexpr int64_t kMaxIndexedRows = (int64_t(1) << 31) - 1;
+// Selection: [N] byte mask, [N] int32 compact positions, [cap] int32 selected row
+// ids in ascending order (-1 past the count), with cap = min(n_rows, N).
+struct SelLayout {
+  int64_t cap = 0;
+  size_t mask_off = 0, pos_off = 0, sel_off = 0, total = 0;
+};
+SelLayout sel_layout(int64_t N, int64_t n_rows);
+// Linear variants: the selection, then the gathered rows (hidden [cap][D] x,
+// targets [cap] int64, temperature [cap], grad_out [cap], lse [cap]), the
+// compact outputs (logp, lse, d_hidden [cap][D]), then the dense workspace.
+struct IdxLayout {
+  SelLayout sel;
+  size_t h_off = 0, t_off = 0, temp_off = 0, g_off = 0, lse_in_off = 0;
+  size_t logp_off = 0, lse_off = 0, dh_off = 0, dense_off = 0;
+};
+IdxLayout idx_layout(int64_t N, int64_t D, int64_t n_rows, flp_dtype x, bool backward,
+                     bool need_dh);
+
 // ---- validation (pure host logic; never dereferences a pointer) ----
 flp_status validate_forward(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
                             const void* hidden, const void* weight, const float* bias,
@@ -83,11 +104,39 @@ flp_status validate_logits_forward(int64_t N, int64_t V, flp_dtype x_dtype, cons
 flp_status validate_logits_backward(int64_t N, int64_t V, flp_dtype x_dtype, const float* grad_out,
                                     const float* lse, const void* logits, const void* targets,
                                     flp_dtype t_dtype, const void* d_logits);
+// The row list of an indexed call (shared by every indexed variant).
+flp_status validate_rows(int64_t N, const void* rows, flp_dtype r_dtype, int64_t n_rows);
 flp_status validate_backward(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
                              const float* grad_out, const float* lse,
                              const void* hidden, const void* weight, const float* bias,
                              const void* targets, flp_dtype t_dtype, const float* temperature,
                              const void* d_hidden, const void* d_weight, flp_dtype dw_dtype,
                              const float* d_bias, const void* workspace, size_t workspace_bytes);
+
+// Indexed variants: the dense gates plus the row list and the indexed workspace.
+flp_status validate_forward_indexed(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
+                                    const void* hidden, const void* weight, const float* bias,
+                                    const void* targets, flp_dtype t_dtype,
+                                    const float* temperature, const void* rows,
+                                    flp_dtype r_dtype, int64_t n_rows, const float* out_logp,
+                                    const float* out_lse, const void* workspace,
+                                    size_t workspace_bytes);
+flp_status validate_backward_indexed(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
+                                     const float* grad_out, const float* lse,
+                                     const void* hidden, const void* weight, const float* bias,
+                                     const void* targets, flp_dtype t_dtype,
+                                     const float* temperature, const void* rows,
+                                     flp_dtype r_dtype, int64_t n_rows, const void* d_hidden,
+                                     const void* d_weight, flp_dtype dw_dtype,
+                                     const float* d_bias, const void* workspace,
+                                     size_t workspace_bytes);
+// Forward (backward = false): out_a = logp [N], out_b = lse [N] or NULL.
+// Backward: out_a = d_logits [N, V], out_b = NULL.
+flp_status validate_logits_indexed(int64_t N, int64_t V, flp_dtype x_dtype, bool backward,
+                                   const float* grad_out, const float* lse, const void* logits,
+                                   const void* targets, flp_dtype t_dtype, const void* rows,
+                                   flp_dtype r_dtype, int64_t n_rows, const void* out_a,
+                                   const void* out_b, const void* workspace,
+                                   size_t workspace_bytes);
 
 }  // namespace flp

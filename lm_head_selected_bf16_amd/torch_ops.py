@@ -290,3 +290,166 @@ class LogitsLogp(torch.autograd.Function):
 def logits_logp(logits, targets):
     """logp[..] = log_softmax(logits)[target], 0 for out-of-range targets (differentiable)."""
     return LogitsLogp.apply(logits, targets)
+
+
+# ---- indexed (row-subset) variants ------------------------------------------------------------
+#
+# rows: 1-D int64 / int32 ids into the flattened batch (PR #547 "What", indexed
+# semantics): outputs keep the full row shape, a duplicated id selects its row
+# once, ids outside [0, N) are ignored, rows left out get logp = lse = 0 and zero
+# gradients; d_weight and d_bias sum over the selected rows.
+
+def _prepare_rows(rows: torch.Tensor, dev: torch.device):
+    if rows.dtype not in _T_DTYPES:
+        raise TypeError("rows must be int64 or int32")
+    if rows.dim() != 1 or not rows.is_contiguous() or rows.device != dev:
+        raise ValueError("rows must be a contiguous 1-D tensor on the inputs' device")
+    return rows, int(rows.shape[0]), _T_DTYPES[rows.dtype]
+
+
+def forward_indexed(hidden: torch.Tensor, weight: torch.Tensor, targets: torch.Tensor,
+                    rows: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                    temperature: Optional[torch.Tensor] = None, return_lse: bool = True
+                    ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """logp (and lse) of the selected rows, zeros elsewhere, through flp_forward_indexed."""
+    h2, t1, temp1, lead, N, D, V = _prepare(hidden, weight, targets, bias, temperature)
+    dev = hidden.device
+    rows, n_rows, r_dt = _prepare_rows(rows, dev)
+    logp = torch.empty(lead, dtype=torch.float32, device=dev)
+    lse = torch.empty(lead, dtype=torch.float32, device=dev) if return_lse else None
+    need = _abi.flp_forward_indexed_workspace_bytes(N, D, V, _X_DTYPES[hidden.dtype], n_rows)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    st = _abi.flp_forward_indexed(N, D, V, _X_DTYPES[hidden.dtype], _ptr(h2), _ptr(weight),
+                                  _ptr(bias), _ptr(t1), _T_DTYPES[targets.dtype], _ptr(temp1),
+                                  _ptr(rows), r_dt, n_rows, _ptr(logp), _ptr(lse), _ptr(ws),
+                                  ws.numel(), _stream(dev))
+    _check("flp_forward_indexed", st)
+    return logp, lse
+
+
+def backward_indexed(grad_out: torch.Tensor, lse: torch.Tensor, hidden: torch.Tensor,
+                     weight: torch.Tensor, targets: torch.Tensor, rows: torch.Tensor,
+                     bias: Optional[torch.Tensor] = None,
+                     temperature: Optional[torch.Tensor] = None, need_hidden: bool = True,
+                     need_weight: bool = True, need_bias: Optional[bool] = None,
+                     dw_dtype: Optional[torch.dtype] = None,
+                     workspace_bytes: Optional[int] = None):
+    """(d_hidden, d_weight, d_bias) of the selected rows through flp_backward_indexed."""
+    h2, t1, temp1, lead, N, D, V = _prepare(hidden, weight, targets, bias, temperature)
+    dev = hidden.device
+    rows, n_rows, r_dt = _prepare_rows(rows, dev)
+    if need_bias is None:
+        need_bias = bias is not None
+    for name, x in (("grad_out", grad_out), ("lse", lse)):
+        if x.dtype != torch.float32 or tuple(x.shape) != lead or not x.is_contiguous():
+            raise ValueError(f"{name} must be contiguous float32 with the targets shape")
+    dwt = hidden.dtype if dw_dtype is None else dw_dtype
+    xd, wd = _X_DTYPES[hidden.dtype], _X_DTYPES[dwt]
+    d_hidden = torch.empty_like(hidden) if need_hidden else None
+    d_weight = torch.empty(weight.shape, dtype=dwt, device=dev) if need_weight else None
+    d_bias = torch.empty(V, dtype=torch.float32, device=dev) if need_bias else None
+    if workspace_bytes is None:
+        cap = max(min(n_rows, N), 1)
+        workspace_bytes = _abi.flp_backward_indexed_workspace_bytes(N, D, V, xd, wd, n_rows, cap)
+        if workspace_bytes > DEFAULT_BWD_WORKSPACE:
+            workspace_bytes = max(DEFAULT_BWD_WORKSPACE,
+                                  _abi.flp_backward_indexed_workspace_bytes(N, D, V, xd, wd,
+                                                                            n_rows, 0))
+    ws = torch.empty(max(int(workspace_bytes), 16), dtype=torch.uint8, device=dev)
+    st = _abi.flp_backward_indexed(N, D, V, xd, _ptr(grad_out), _ptr(lse), _ptr(h2),
+                                   _ptr(weight), _ptr(bias), _ptr(t1), _T_DTYPES[targets.dtype],
+                                   _ptr(temp1), _ptr(rows), r_dt, n_rows, _ptr(d_hidden),
+                                   _ptr(d_weight), wd, _ptr(d_bias), _ptr(ws), ws.numel(),
+                                   _stream(dev))
+    _check("flp_backward_indexed", st)
+    return d_hidden, d_weight, d_bias
+
+
+class LinearLogpIndexed(torch.autograd.Function):
+    """Autograd node of the indexed linear operator; the forward saves lse."""
+
+    @staticmethod
+    def forward(ctx, hidden, weight, targets, rows, bias, temperature):
+        logp, lse = forward_indexed(hidden, weight, targets, rows, bias, temperature)
+        ctx.save_for_backward(hidden, weight, targets, rows, bias, temperature, lse)
+        ctx.mark_non_differentiable(lse)
+        return logp, lse
+
+    @staticmethod
+    def backward(ctx, g_logp, g_lse):
+        hidden, weight, targets, rows, bias, temperature, lse = ctx.saved_tensors
+        need_h, need_w, _, _, need_b, _ = ctx.needs_input_grad
+        if not (need_h or need_w or need_b):
+            return None, None, None, None, None, None
+        dh, dw, db = backward_indexed(g_logp.contiguous().to(torch.float32), lse, hidden, weight,
+                                      targets, rows, bias, temperature, need_hidden=need_h,
+                                      need_weight=need_w,
+                                      need_bias=bool(need_b and bias is not None))
+        return dh, dw, None, None, db, None
+
+
+def linear_logp_indexed(hidden, weight, targets, rows, bias=None, temperature=None):
+    """linear_logp restricted to the rows listed in ``rows`` (full shape, zeros elsewhere)."""
+    return LinearLogpIndexed.apply(hidden, weight, targets, rows, bias, temperature)[0]
+
+
+def logits_forward_indexed(logits: torch.Tensor, targets: torch.Tensor, rows: torch.Tensor,
+                           return_lse: bool = True
+                           ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """logp (and lse) of the selected rows of given logits through flp_logits_forward_indexed."""
+    z2, t1, lead, N, V = _prepare_logits(logits, targets)
+    dev = logits.device
+    rows, n_rows, r_dt = _prepare_rows(rows, dev)
+    logp = torch.empty(lead, dtype=torch.float32, device=dev)
+    lse = torch.empty(lead, dtype=torch.float32, device=dev) if return_lse else None
+    ws = torch.empty(max(_abi.flp_logits_indexed_workspace_bytes(N), 16), dtype=torch.uint8,
+                     device=dev)
+    st = _abi.flp_logits_forward_indexed(N, V, _X_DTYPES[logits.dtype], _ptr(z2), _ptr(t1),
+                                         _T_DTYPES[targets.dtype], _ptr(rows), r_dt, n_rows,
+                                         _ptr(logp), _ptr(lse), _ptr(ws), ws.numel(), _stream(dev))
+    _check("flp_logits_forward_indexed", st)
+    return logp, lse
+
+
+def logits_backward_indexed(grad_out: torch.Tensor, lse: torch.Tensor, logits: torch.Tensor,
+                            targets: torch.Tensor, rows: torch.Tensor) -> torch.Tensor:
+    """d logits of the selected rows (zero rows elsewhere) through flp_logits_backward_indexed."""
+    z2, t1, lead, N, V = _prepare_logits(logits, targets)
+    dev = logits.device
+    rows, n_rows, r_dt = _prepare_rows(rows, dev)
+    for name, x in (("grad_out", grad_out), ("lse", lse)):
+        if x.dtype != torch.float32 or tuple(x.shape) != lead or not x.is_contiguous():
+            raise ValueError(f"{name} must be contiguous float32 with the targets shape")
+    d = torch.empty_like(logits)
+    ws = torch.empty(max(_abi.flp_logits_indexed_workspace_bytes(N), 16), dtype=torch.uint8,
+                     device=dev)
+    st = _abi.flp_logits_backward_indexed(N, V, _X_DTYPES[logits.dtype], _ptr(grad_out),
+                                          _ptr(lse), _ptr(z2), _ptr(t1), _T_DTYPES[targets.dtype],
+                                          _ptr(rows), r_dt, n_rows, _ptr(d), _ptr(ws), ws.numel(),
+                                          _stream(dev))
+    _check("flp_logits_backward_indexed", st)
+    return d
+
+
+class LogitsLogpIndexed(torch.autograd.Function):
+    """Autograd node of the indexed operator on materialised logits."""
+
+    @staticmethod
+    def forward(ctx, logits, targets, rows):
+        logp, lse = logits_forward_indexed(logits, targets, rows, return_lse=True)
+        ctx.save_for_backward(logits, targets, rows, lse)
+        return logp
+
+    @staticmethod
+    def backward(ctx, g_logp):
+        logits, targets, rows, lse = ctx.saved_tensors
+        if not ctx.needs_input_grad[0]:
+            return None, None, None
+        d = logits_backward_indexed(g_logp.contiguous().to(torch.float32), lse, logits, targets,
+                                    rows)
+        return d, None, None
+
+
+def logits_logp_indexed(logits, targets, rows):
+    """logits_logp restricted to the rows listed in ``rows`` (full shape, zeros elsewhere)."""
+    return LogitsLogpIndexed.apply(logits, targets, rows)

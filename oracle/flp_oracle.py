@@ -32,7 +32,9 @@ Sources (the pages this follows):
     grad_out * (one_hot(token) - softmax(logits)); its inline review: labels
     below zero or at least the vocabulary size give the 0 result.
   * PR #547 page (deterministic LogP autograd), section "What", "Indexed
-    semantics": out-of-range tokens are ignored and have zero derivatives.
+    semantics": out-of-range tokens are ignored and have zero derivatives;
+    the indexed variants keep the full row shape, select a duplicated row id
+    once, ignore out-of-range ids and give unselected rows zero derivatives.
 
 Readings where the pages leave a step open (also listed with the rest of the
 design notes):
@@ -62,6 +64,11 @@ __all__ = [
     "backward",
     "logits_forward",
     "logits_backward",
+    "selected_rows",
+    "forward_indexed",
+    "backward_indexed",
+    "logits_forward_indexed",
+    "logits_backward_indexed",
 ]
 
 
@@ -242,4 +249,64 @@ def logits_backward(logits_in, targets, grad_out, rows=None, chunk=512):
         r = idx[s:s + chunk]
         l = row_lse(Z[r])
         out[s:s + chunk] = dlogits(Z[r], l, t[r], g[r])
+    return out
+
+
+# ---- indexed (row-subset) variants ------------------------------------------------------------
+#
+# PR #547 page, section "What", indexed semantics: the outputs keep the full row
+# shape; an id listed more than once selects its row once; an id outside the
+# batch is ignored; rows that are not selected have zero derivatives.  PR #234,
+# "Implementation details": rows left out by an indexed call get exactly zero
+# gradients.  Reading adopted for the forward outputs of rows left out: logp and
+# lse are 0 (the allocating variant's zero-filled output).
+
+def selected_rows(n_rows_total, ids):
+    """The rows an id list selects: the distinct ids in [0, n_rows_total), ascending."""
+    r = _as_i64(ids).reshape(-1)
+    r = r[(r >= 0) & (r < n_rows_total)]
+    return np.unique(r)
+
+
+def forward_indexed(hidden, weight, targets, ids, bias=None, temperature=None, chunk=512):
+    """(logp, lse) [N] float64: the dense oracle on the selected rows, 0 elsewhere."""
+    N = int(hidden.shape[0])
+    s = selected_rows(N, ids)
+    logp, lse = np.zeros(N), np.zeros(N)
+    if s.size:
+        logp[s], lse[s] = forward(hidden, weight, targets, bias, temperature, rows=s, chunk=chunk)
+    return logp, lse
+
+
+def backward_indexed(hidden, weight, targets, grad_out, ids, bias=None, temperature=None,
+                     chunk=512):
+    """(d_hidden [N, D], d_weight [V, D], d_bias [V]) float64: the dense oracle on the selected
+    rows; d_hidden rows left out are 0, d_weight and d_bias sum over the selected rows."""
+    N, D = int(hidden.shape[0]), int(hidden.shape[1])
+    V = int(weight.shape[0])
+    s = selected_rows(N, ids)
+    d_hidden, d_weight, d_bias = np.zeros((N, D)), np.zeros((V, D)), np.zeros(V)
+    if s.size:
+        d_hidden[s], d_weight, d_bias = backward(hidden, weight, targets, grad_out, bias,
+                                                 temperature, rows=s, chunk=chunk)
+    return d_hidden, d_weight, d_bias
+
+
+def logits_forward_indexed(logits_in, targets, ids, chunk=512):
+    """(logp, lse) [N] float64 of given logits on the selected rows, 0 elsewhere."""
+    N = int(logits_in.shape[0])
+    s = selected_rows(N, ids)
+    logp, lse = np.zeros(N), np.zeros(N)
+    if s.size:
+        logp[s], lse[s] = logits_forward(logits_in, targets, rows=s, chunk=chunk)
+    return logp, lse
+
+
+def logits_backward_indexed(logits_in, targets, grad_out, ids, chunk=512):
+    """d logits [N, V] float64 on the selected rows, zero rows elsewhere."""
+    N, V = int(logits_in.shape[0]), int(logits_in.shape[1])
+    s = selected_rows(N, ids)
+    out = np.zeros((N, V))
+    if s.size:
+        out[s] = logits_backward(logits_in, targets, grad_out, rows=s, chunk=chunk)
     return out

@@ -337,4 +337,77 @@ def pin_logits_op_finite_differences(o):
     assert np.linalg.norm(num - an) / np.linalg.norm(an) < 1e-6
 
 
+# ---- indexed (row-subset) variants ---------------------------------------------------------
+
+_IDS = np.array([3, -1, 3, 0, 7, 0, -6])  # selects rows {0, 3} of 5; -1 / -6 / 7 are ignored
+
+
+def pin_indexed_library(o):
+    """Indexed forward/backward against scipy's log_softmax and torch autograd of the loss
+    sum over the selected rows {0, 3} of g_i logp_i (rows 1, 2, 4 left out: zeros)."""
+    H, W, b, T, t = _case(50, N=5, D=3, V=4)
+    g = _rng(51).standard_normal(5)
+    sel = np.array([0, 3])
+    Z = (H @ W.T + b[None, :]) / T[:, None]
+    ls = scipy.special.log_softmax(Z, axis=1)
+    want = np.zeros(5)
+    want[sel] = ls[sel, t[sel]]
+    want_lse = np.zeros(5)
+    want_lse[sel] = scipy.special.logsumexp(Z[sel], axis=1)
+    lp, lse = o.forward_indexed(H, W, t, _IDS, bias=b, temperature=T)
+    assert np.max(np.abs(lp - want)) < 1e-12 and np.max(np.abs(lse - want_lse)) < 1e-12
+    assert np.all(lp[[1, 2, 4]] == 0.0) and np.all(lse[[1, 2, 4]] == 0.0)
+    Ht = torch.tensor(H, requires_grad=True)
+    Wt = torch.tensor(W, requires_grad=True)
+    bt = torch.tensor(b, requires_grad=True)
+    z = (Ht @ Wt.T + bt) / torch.tensor(T)[:, None]
+    L = (torch.log_softmax(z, dim=1)[sel, t[sel]] * torch.tensor(g[sel])).sum()
+    L.backward()
+    dh, dw, db = o.backward_indexed(H, W, t, g, _IDS, bias=b, temperature=T)
+    assert np.max(np.abs(dh - Ht.grad.numpy())) < 1e-12
+    assert np.all(dh[[1, 2, 4]] == 0.0)
+    assert np.max(np.abs(dw - Wt.grad.numpy())) < 1e-12
+    assert np.max(np.abs(db - bt.grad.numpy())) < 1e-12
+
+
+def pin_indexed_id_lists(o):
+    """The selection is a set: any order, repeats and out-of-range ids give the same result as
+    the ascending distinct ids; all ids give the dense result; no ids give zeros."""
+    H, W, b, T, t = _case(52, N=6, D=4, V=5)
+    g = _rng(53).standard_normal(6)
+    base = o.backward_indexed(H, W, t, g, np.array([1, 4]), bias=b, temperature=T)
+    for ids in ([4, 1], [4, 4, 1, 1, 4], [-1, 4, 6, 1, -7, 100]):
+        got = o.backward_indexed(H, W, t, g, np.array(ids), bias=b, temperature=T)
+        assert all(np.array_equal(x, y) for x, y in zip(got, base)), ids
+    # all rows: the dense forward (closed form via scipy) and the dense backward
+    Z = (H @ W.T + b[None, :]) / T[:, None]
+    lp, _ = o.forward_indexed(H, W, t, np.arange(6)[::-1], bias=b, temperature=T)
+    assert np.max(np.abs(lp - scipy.special.log_softmax(Z, axis=1)[np.arange(6), t])) < 1e-12
+    # nothing selected
+    lp, lse = o.forward_indexed(H, W, t, np.array([], dtype=np.int64), bias=b, temperature=T)
+    dh, dw, db = o.backward_indexed(H, W, t, g, np.array([-2, 6]), bias=b, temperature=T)
+    assert not lp.any() and not lse.any() and not dh.any() and not dw.any() and not db.any()
+
+
+def pin_logits_indexed_library(o):
+    """Indexed operator on given logits against scipy and torch autograd on the selected rows."""
+    r = _rng(54)
+    Z = r.standard_normal((5, 7)) * 2.0
+    t = np.array([1, 6, -1, 3, 9])
+    g = r.standard_normal(5)
+    sel = np.array([0, 3])  # _IDS selects rows 0 and 3
+    ls = scipy.special.log_softmax(Z, axis=1)
+    lp, lse = o.logits_forward_indexed(Z, t, _IDS)
+    want = np.zeros(5)
+    want[sel] = ls[sel, t[sel]]
+    assert np.max(np.abs(lp - want)) < 1e-12
+    assert np.max(np.abs(lse[sel] - scipy.special.logsumexp(Z[sel], axis=1))) < 1e-12
+    assert np.all(lse[[1, 2, 4]] == 0.0)
+    Zt = torch.tensor(Z, requires_grad=True)
+    (torch.log_softmax(Zt, dim=1)[sel, t[sel]] * torch.tensor(g[sel])).sum().backward()
+    d = o.logits_backward_indexed(Z, t, g, _IDS)
+    assert np.max(np.abs(d - Zt.grad.numpy())) < 1e-12
+    assert np.all(d[[1, 2, 4]] == 0.0)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

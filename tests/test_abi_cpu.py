@@ -238,3 +238,118 @@ def lbwd(**kw):
 ])
 def test_logits_backward_gates(kw, expect):
     assert abi.STATUS_NAMES[lbwd(**kw)] == expect
+
+
+# ---- indexed variants ----
+RW = 0xC0000000  # row ids
+
+
+def ifwd(**kw):
+    a = dict(N=N, D=D, V=V, x=BF16, hidden=H, weight=W, bias=B, targets=T, t=I64, temp=TMP,
+             rows=RW, r=I64, n=17, logp=LP, lse=LS, ws=WS,
+             wsb=abi.flp_forward_indexed_workspace_bytes(N, D, V, BF16, 17), stream=0)
+    a.update(kw)
+    return abi.flp_forward_indexed(a["N"], a["D"], a["V"], a["x"], a["hidden"], a["weight"],
+                                   a["bias"], a["targets"], a["t"], a["temp"], a["rows"], a["r"],
+                                   a["n"], a["logp"], a["lse"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(n=-1), "FLP_INVALID_ARGUMENT"),
+    (dict(r=BF16), "FLP_UNSUPPORTED_DTYPE"),
+    (dict(rows=0), "FLP_INVALID_ARGUMENT"),             # ids required when n_rows > 0
+    (dict(rows=RW + 4), "FLP_MISALIGNED"),              # int64 ids 8-byte aligned
+    (dict(rows=LP), "FLP_INVALID_ARGUMENT"),            # ids overlap an output
+    (dict(rows=WS + 256), "FLP_INVALID_ARGUMENT"),      # ids inside the workspace
+    (dict(N=1 << 31), "FLP_UNSUPPORTED_SHAPE"),         # compact positions are int32
+    (dict(D=48), "FLP_UNSUPPORTED_SHAPE"),
+    (dict(wsb=1024), "FLP_WORKSPACE_TOO_SMALL"),
+    (dict(ws=0), "FLP_INVALID_ARGUMENT"),
+    (dict(N=0, hidden=0, targets=0, logp=0, ws=0), "FLP_OK"),
+])
+def test_forward_indexed_gates(kw, expect):
+    assert abi.STATUS_NAMES[ifwd(**kw)] == expect
+
+
+def ibwd(**kw):
+    a = dict(N=N, D=D, V=V, x=BF16, g=TMP, lse=LS, hidden=H, weight=W, bias=B, targets=T, t=I64,
+             temp=0, rows=RW, r=I32, n=9, dh=0x90000000, dw=0xA0000000, dwt=BF16, db=0xB0000000,
+             ws=WS, wsb=abi.flp_backward_indexed_workspace_bytes(N, D, V, BF16, BF16, 9, 0),
+             stream=0)
+    a.update(kw)
+    return abi.flp_backward_indexed(a["N"], a["D"], a["V"], a["x"], a["g"], a["lse"], a["hidden"],
+                                    a["weight"], a["bias"], a["targets"], a["t"], a["temp"],
+                                    a["rows"], a["r"], a["n"], a["dh"], a["dw"], a["dwt"], a["db"],
+                                    a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(n=-2), "FLP_INVALID_ARGUMENT"),
+    (dict(r=F32), "FLP_UNSUPPORTED_DTYPE"),
+    (dict(rows=RW + 2), "FLP_MISALIGNED"),              # int32 ids 4-byte aligned
+    (dict(rows=0xA0000000 + 4096), "FLP_INVALID_ARGUMENT"),  # ids inside d_weight
+    (dict(x=F32, dwt=BF16), "FLP_UNSUPPORTED_DTYPE"),
+    (dict(g=0), "FLP_INVALID_ARGUMENT"),
+    (dict(wsb=4096), "FLP_WORKSPACE_TOO_SMALL"),
+    (dict(dh=0, dw=0, db=0, ws=0), "FLP_OK"),           # nothing requested: no-op
+    (dict(N=0, g=0, lse=0, hidden=0, targets=0, ws=0), "FLP_OK"),
+])
+def test_backward_indexed_gates(kw, expect):
+    assert abi.STATUS_NAMES[ibwd(**kw)] == expect
+
+
+def test_indexed_workspace_sizes():
+    # the prefix (mask, positions, ids, gathered rows) plus the dense workspace of min(n, N) rows
+    f = abi.flp_forward_indexed_workspace_bytes(1000, 2688, 131072, BF16, 300)
+    assert f > abi.flp_forward_workspace_bytes(300, 2688, 131072) + 300 * 2688 * 2
+    assert (abi.flp_forward_indexed_workspace_bytes(1000, 2688, 131072, BF16, 5000) ==
+            abi.flp_forward_indexed_workspace_bytes(1000, 2688, 131072, BF16, 1000))
+    assert abi.flp_forward_indexed_workspace_bytes(1000, 2688, 131072, BF16, 0) < 8192
+    b = abi.flp_backward_indexed_workspace_bytes(1000, 2688, 131072, BF16, BF16, 300, 300)
+    assert b > abi.flp_backward_workspace_bytes(300, 2688, 131072, BF16, BF16, 300)
+    assert abi.flp_logits_indexed_workspace_bytes(1000) == 1024
+    assert abi.flp_logits_indexed_workspace_bytes(0) == 0
+
+
+def lifwd(**kw):
+    a = dict(N=N, V=1024, x=BF16, z=WS, targets=T, t=I64, rows=RW, r=I64, n=5, logp=LP, lse=LS,
+             ws=0x90000000, wsb=256, stream=0)
+    a.update(kw)
+    return abi.flp_logits_forward_indexed(a["N"], a["V"], a["x"], a["z"], a["targets"], a["t"],
+                                          a["rows"], a["r"], a["n"], a["logp"], a["lse"], a["ws"],
+                                          a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(n=-1), "FLP_INVALID_ARGUMENT"),
+    (dict(r=F32), "FLP_UNSUPPORTED_DTYPE"),
+    (dict(rows=0), "FLP_INVALID_ARGUMENT"),
+    (dict(ws=0), "FLP_INVALID_ARGUMENT"),
+    (dict(wsb=16), "FLP_WORKSPACE_TOO_SMALL"),          # one mask byte per row, 256-rounded
+    (dict(ws=LP), "FLP_INVALID_ARGUMENT"),              # workspace overlaps logp
+    (dict(V=1001), "FLP_UNSUPPORTED_SHAPE"),
+    (dict(N=0, z=0, targets=0, logp=0, ws=0), "FLP_OK"),
+])
+def test_logits_forward_indexed_gates(kw, expect):
+    assert abi.STATUS_NAMES[lifwd(**kw)] == expect
+
+
+def libwd(**kw):
+    a = dict(N=N, V=1024, x=BF16, g=TMP, lse=LS, z=WS, targets=T, t=I32, rows=RW, r=I32, n=5,
+             d=0x90000000, ws=0xB0000000, wsb=256, stream=0)
+    a.update(kw)
+    return abi.flp_logits_backward_indexed(a["N"], a["V"], a["x"], a["g"], a["lse"], a["z"],
+                                           a["targets"], a["t"], a["rows"], a["r"], a["n"], a["d"],
+                                           a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(g=0), "FLP_INVALID_ARGUMENT"),
+    (dict(lse=0), "FLP_INVALID_ARGUMENT"),
+    (dict(d=0x90000008), "FLP_MISALIGNED"),
+    (dict(rows=0x90000000 + 64), "FLP_INVALID_ARGUMENT"),  # ids inside d_logits
+    (dict(wsb=0), "FLP_WORKSPACE_TOO_SMALL"),
+    (dict(N=0, g=0, lse=0, z=0, targets=0, d=0, ws=0), "FLP_OK"),
+])
+def test_logits_backward_indexed_gates(kw, expect):
+    assert abi.STATUS_NAMES[libwd(**kw)] == expect

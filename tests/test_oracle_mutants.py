@@ -7,7 +7,8 @@ import pytest
 import oracle.flp_oracle as O
 from oracle_pins import ALL_PINS
 
-_orig = {k: getattr(O, k) for k in ("logits", "row_lse", "valid_mask", "select_logp", "dlogits")}
+_orig = {k: getattr(O, k) for k in ("logits", "row_lse", "valid_mask", "select_logp", "dlogits",
+                                     "selected_rows")}
 
 
 def _logits_no_bias(H, W, bias=None, temperature=None):
@@ -107,6 +108,21 @@ def _dlogits_temp_squared(Z, lse, t, g, temperature=None):
     return d if temperature is None else d / temperature[:, None]
 
 
+def _sel_keeps_duplicates(n, ids):
+    r = np.asarray(ids, dtype=np.int64).reshape(-1)
+    return np.sort(r[(r >= 0) & (r < n)])
+
+
+def _sel_wraps_negative(n, ids):
+    r = np.asarray(ids, dtype=np.int64).reshape(-1)
+    return np.unique(r[(r >= -n) & (r < n)] % n)
+
+
+def _sel_off_by_one(n, ids):
+    r = np.asarray(ids, dtype=np.int64).reshape(-1)
+    return np.unique(r[(r >= 0) & (r <= n)] % n)
+
+
 MUTANTS = {
     "logits_no_bias": ("logits", _logits_no_bias),
     "logits_temp_multiplies": ("logits", _logits_temp_mul),
@@ -125,6 +141,9 @@ MUTANTS = {
     "dlogits_missing_onehot": ("dlogits", _dlogits_no_onehot),
     "dlogits_ignored_rows_not_zeroed": ("dlogits", _dlogits_no_rowmask),
     "dlogits_T_twice": ("dlogits", _dlogits_temp_squared),
+    "selection_keeps_duplicate_ids": ("selected_rows", _sel_keeps_duplicates),
+    "selection_wraps_negative_ids": ("selected_rows", _sel_wraps_negative),
+    "selection_accepts_id_N": ("selected_rows", _sel_off_by_one),
 }
 
 
