@@ -369,6 +369,61 @@ def indexed_step(name: str, n_sel: int, steps: int, warmup: int):
     return out
 
 
+def embedding_op(N: int, D: int, V: int, steps: int, warmup: int):
+    """The untied embedding lookup and its sorted-segment grad_weight at the model row's
+    shape (HBM-bound: the lookup reads and writes N rows; the backward reads N gradient
+    rows and writes all V rows of d_weight)."""
+    import torch
+
+    import flp_inputs
+    import lm_head_selected_bf16_amd as m
+
+    inp = flp_inputs.make_embedding_inputs(N, D, V, torch.bfloat16, 52, ids="zipf",
+                                           device="cuda:0")
+    w, g, ids = inp["weight"], inp["grad"], inp["ids"].cuda()
+    out = torch.empty(N, D, dtype=torch.bfloat16, device="cuda:0")
+    dw = torch.empty_like(w)
+    ws = torch.empty(m.flp_embedding_backward_workspace_bytes(N, D, V), dtype=torch.uint8,
+                     device="cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    fwd_ms, bwd_ms = [], []
+
+    def call(timed):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        st = m.flp_embedding_forward(N, D, V, m.FLP_BF16, w.data_ptr(), ids.data_ptr(),
+                                     m.FLP_I64, out.data_ptr(), stream)
+        e[1].record()
+        st2 = m.flp_embedding_backward(N, D, V, m.FLP_BF16, g.data_ptr(), ids.data_ptr(),
+                                       m.FLP_I64, dw.data_ptr(), m.FLP_BF16, ws.data_ptr(),
+                                       ws.numel(), stream)
+        e[2].record()
+        if st != m.FLP_OK or st2 != m.FLP_OK:
+            raise m.FlpError("flp_embedding_forward / flp_embedding_backward", st or st2)
+        if timed:
+            torch.cuda.synchronize()
+            fwd_ms.append(e[0].elapsed_time(e[1]))
+            bwd_ms.append(e[1].elapsed_time(e[2]))
+
+    for _ in range(warmup):
+        call(False)
+    for _ in range(steps):
+        call(True)
+    f, b = sorted(fwd_ms)[len(fwd_ms) // 2], sorted(bwd_ms)[len(bwd_ms) // 2]
+    fb = 2 * N * D * 2 + N * 8
+    bb = N * D * 2 + V * D * 2 + N * 8
+    res = {"workload": f"embedding_n{N}: untied bf16 table [{V}, {D}], zipf-drawn ids; lookup "
+                       f"and sorted-segment d_weight (bf16, fp32 accumulation)",
+           "distinct_ids": int(torch.unique(ids).numel())}
+    for kind, ms, byts in (("forward", f, fb), ("backward", b, bb)):
+        gbs = byts / (ms / 1e3) / 1e9
+        res[kind] = {"ms": round(ms, 4), "bound": "hbm", "algorithmic_bytes": byts,
+                     "achieved_GBs": round(gbs, 1), "peak_GBs": PEAK_HBM_GBS,
+                     "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    del w, g, out, dw, ws
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -468,6 +523,9 @@ def main() -> int:
         torch.cuda.empty_cache()
         log("indexed: half of train_n16384's rows")
         out["train_n16384_indexed_half"] = indexed_step(name, N // 2, 5, 2)
+        torch.cuda.empty_cache()
+        log("untied embedding lookup: N=16384, D=2688, V=131072")
+        out["embedding_n16384"] = embedding_op(16384, 2688, 131072, 10, 3)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         cpu_prob = Problem.__new__(Problem)

@@ -157,6 +157,33 @@ def make_logits_inputs(name: str, N: int, V: int, dtype: torch.dtype, seed: int,
     return dict(workload=w, logits=z.to(dtype), targets=draw_targets(w), grad_out=draw_grad(w))
 
 
+def make_embedding_inputs(N: int, D: int, V: int, dtype: torch.dtype, seed: int,
+                          ids: str = "zipf", invalid: Tuple[int, ...] = (),
+                          device: str = "cpu"):
+    """Inputs of the untied embedding lookup: a table E ~ N(0, 0.02^2) [V, D] in `dtype`
+    (drawn on `device`), token ids [N] int64 and an upstream gradient [N, D] ~ N(0, 1) in
+    `dtype`.  ids = "zipf": a heavy-headed token-frequency draw, floor(V^u) - 1 for u
+    uniform (many repeats of the frequent ids, most ids absent); "uniform": uniform over
+    [0, V); "same": every token has id V // 2.  The given out-of-range values replace
+    the first len(invalid) ids."""
+    g = torch.Generator(device=device)
+    g.manual_seed(1000 * seed)
+    E = torch.empty(V, D, dtype=torch.float32, device=device).normal_(0.0, 0.02, generator=g)
+    gc = torch.Generator(device="cpu")
+    gc.manual_seed(1000 * seed + 1)
+    if ids == "zipf":
+        u = torch.rand(N, generator=gc, dtype=torch.float64)
+        t = (torch.floor(torch.pow(float(V), u)) - 1).clamp_(0, V - 1).to(torch.int64)
+    elif ids == "uniform":
+        t = torch.randint(0, V, (N,), generator=gc)
+    else:
+        t = torch.full((N,), V // 2, dtype=torch.int64)
+    if invalid:
+        t[:len(invalid)] = torch.tensor(invalid, dtype=torch.int64)
+    grad = torch.empty(N, D, dtype=torch.float32, device=device).normal_(0.0, 1.0, generator=g)
+    return dict(weight=E.to(dtype), ids=t, grad=grad.to(dtype))
+
+
 def random_rows(n_total: int, k: int, seed: int) -> torch.Tensor:
     """A seeded sorted sample of k distinct row indices out of n_total."""
     g = torch.Generator(device="cpu")

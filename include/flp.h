@@ -284,6 +284,41 @@ flp_status flp_logits_backward_indexed(int64_t N, int64_t V, flp_dtype x_dtype,
                                        size_t workspace_bytes, void* stream);
 
 /*
+ * Untied embedding lookup ("Feat/nemotron h lm head logprob cuda", PR #555
+ * summary bullets: the untied embedding lookup of the same model row, with a
+ * sorted-segment deterministic grad_weight; its Known issues: the pages'
+ * version accumulates repeated ids in BF16 and misses FP64 parity, so here each
+ * segment accumulates in fp32 and is rounded once).
+ *
+ *   out[i]    = weight[ids[i]]                        [N, D] x_dtype
+ *   d_weight  = sum over i with ids[i] == v of grad[i], summed in ascending i
+ *
+ *   x_dtype   FLP_BF16, FLP_F16 or FLP_F32 (weight, out, grad); D * element
+ *             size must be a multiple of 16.
+ *   ids       [N] of id_dtype (FLP_I64 or FLP_I32).  An id outside [0, V)
+ *             reads as a zero row and contributes no gradient.
+ *   d_weight  [V, D] of dw_dtype (x_dtype or FLP_F32); every row is written
+ *             (zero for ids that do not occur).
+ *   workspace >= flp_embedding_backward_workspace_bytes(N, D, V): radix-sort
+ *             buffers, per-id segment bounds and fp32 pieces of segments that
+ *             span several 32-position groups of the sorted list.
+ *
+ * The backward sorts (id, token) pairs with a stable radix sort and sums each
+ * id's segment in fp32 in a fixed order (token order inside each group of 32
+ * sorted positions, groups in ascending order): d_weight is bitwise
+ * reproducible.  N < 2^31,
+ * V < 2^31 - 1.
+ */
+flp_status flp_embedding_forward(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
+                                 const void* weight, const void* ids, flp_dtype id_dtype,
+                                 void* out, void* stream);
+size_t flp_embedding_backward_workspace_bytes(int64_t N, int64_t D, int64_t V);
+flp_status flp_embedding_backward(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
+                                  const void* grad, const void* ids, flp_dtype id_dtype,
+                                  void* d_weight, flp_dtype dw_dtype, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/*
  * Optional per-kernel timing with HIP events, for benchmarks.  While enabled,
  * every kernel the library enqueues is bracketed by two events recorded on
  * the same stream; flp_profile_read synchronises those events and returns, per
@@ -303,7 +338,8 @@ typedef enum flp_kernel_kind {
   FLP_K_LOGITS_FORWARD = 7,   /* flp_logits_forward */
   FLP_K_LOGITS_BACKWARD = 8,  /* flp_logits_backward */
   FLP_K_ROWS = 9,       /* indexed variants: row selection, gather, scatter */
-  FLP_K_COUNT = 10
+  FLP_K_EMBEDDING = 10, /* flp_embedding_forward / flp_embedding_backward */
+  FLP_K_COUNT = 11
 } flp_kernel_kind;
 
 void flp_profile_enable(int on);

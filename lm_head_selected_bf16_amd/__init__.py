@@ -9,7 +9,9 @@ wrapper with autograd.
 """
 from ._abi import (FLP_BF16, FLP_F16, FLP_F32, FLP_I32, FLP_I64, FLP_OK, FlpError,  # noqa: F401
                    flp_backward, flp_backward_indexed, flp_backward_indexed_workspace_bytes,
-                   flp_backward_workspace_bytes, flp_build_info, flp_forward, flp_forward_indexed,
+                   flp_backward_workspace_bytes, flp_build_info, flp_embedding_backward,
+                   flp_embedding_backward_workspace_bytes, flp_embedding_forward, flp_forward,
+                   flp_forward_indexed,
                    flp_forward_indexed_workspace_bytes, flp_forward_partial,
                    flp_forward_partial_bytes, flp_forward_workspace_bytes, flp_logits_backward,
                    flp_logits_backward_indexed, flp_logits_forward, flp_logits_forward_indexed,
@@ -20,7 +22,8 @@ from .torch_ops import (LinearLogp, backward, backward_workspace_bytes,  # noqa:
                         linear_logp, linear_logp_with_lse, logits_backward, logits_forward,
                         logits_logp, merge, LinearLogpIndexed, LogitsLogpIndexed,
                         backward_indexed, forward_indexed, linear_logp_indexed,
-                        logits_backward_indexed, logits_forward_indexed, logits_logp_indexed)
+                        logits_backward_indexed, logits_forward_indexed, logits_logp_indexed,
+                        Embedding, embedding, embedding_backward, embedding_forward)
 
 __all__ = [
     "FLP_BF16", "FLP_F16", "FLP_F32", "FLP_I32", "FLP_I64", "FLP_OK", "FlpError",
@@ -30,6 +33,7 @@ __all__ = [
     "flp_forward_indexed", "flp_forward_indexed_workspace_bytes", "flp_backward_indexed",
     "flp_backward_indexed_workspace_bytes", "flp_logits_forward_indexed",
     "flp_logits_backward_indexed", "flp_logits_indexed_workspace_bytes",
+    "flp_embedding_forward", "flp_embedding_backward", "flp_embedding_backward_workspace_bytes",
     "flp_status_string", "flp_build_info", "flp_profile_enable", "flp_profile_read", "load",
     "LinearLogp", "forward", "backward", "backward_workspace_bytes",
     "default_backward_workspace_bytes", "linear_logp", "linear_logp_with_lse",
@@ -38,4 +42,5 @@ __all__ = [
     "LinearLogpIndexed", "forward_indexed", "backward_indexed", "linear_logp_indexed",
     "LogitsLogpIndexed", "logits_forward_indexed", "logits_backward_indexed",
     "logits_logp_indexed",
+    "Embedding", "embedding", "embedding_forward", "embedding_backward",
 ]

@@ -53,6 +53,10 @@ SIGNATURES = {
                                           _fp, _vp, _sz, _vp]),
     "flp_logits_backward_indexed": (_int, [_i64, _i64, _int, _fp, _fp, _vp, _vp, _int, _vp, _int,
                                            _i64, _vp, _vp, _sz, _vp]),
+    "flp_embedding_forward": (_int, [_i64, _i64, _i64, _int, _vp, _vp, _int, _vp, _vp]),
+    "flp_embedding_backward_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+    "flp_embedding_backward": (_int, [_i64, _i64, _i64, _int, _vp, _vp, _int, _vp, _int, _vp, _sz,
+                                      _vp]),
     "flp_profile_enable": (None, [_int]),
     "flp_profile_read": (_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64), _int]),
     "flp_status_string": (ctypes.c_char_p, [_int]),
@@ -202,8 +206,24 @@ def flp_logits_backward_indexed(N, V, x_dtype, grad_out, lse, logits, targets, t
                                                   workspace, workspace_bytes, stream))
 
 
+def flp_embedding_forward(N, D, V, x_dtype, weight, ids, id_dtype, out, stream) -> int:
+    """Raw call: every pointer argument is an int address (0 for NULL)."""
+    return int(load().flp_embedding_forward(N, D, V, x_dtype, weight, ids, id_dtype, out, stream))
+
+
+def flp_embedding_backward_workspace_bytes(N: int, D: int, V: int) -> int:
+    return int(load().flp_embedding_backward_workspace_bytes(N, D, V))
+
+
+def flp_embedding_backward(N, D, V, x_dtype, grad, ids, id_dtype, d_weight, dw_dtype, workspace,
+                           workspace_bytes, stream) -> int:
+    """Raw call: every pointer argument is an int address (0 for NULL)."""
+    return int(load().flp_embedding_backward(N, D, V, x_dtype, grad, ids, id_dtype, d_weight,
+                                             dw_dtype, workspace, workspace_bytes, stream))
+
+
 KERNEL_KINDS = ("forward", "merge", "dlogits", "transpose", "d_hidden", "d_weight", "d_bias",
-                "logits_forward", "logits_backward", "rows")
+                "logits_forward", "logits_backward", "rows", "embedding")
 
 
 def flp_profile_enable(on: bool) -> None:

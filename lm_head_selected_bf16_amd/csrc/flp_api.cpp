@@ -516,6 +516,58 @@ flp_status flp_logits_backward_indexed(int64_t N, int64_t V, flp_dtype x_dtype,
   return FLP_OK;
 }
 
+// ---- untied embedding lookup ----
+
+flp_status flp_embedding_forward(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
+                                 const void* weight, const void* ids, flp_dtype id_dtype,
+                                 void* out, void* stream) {
+  flp_status st = validate_embedding_forward(N, D, V, x_dtype, weight, ids, id_dtype, out);
+  if (st != FLP_OK || N == 0) return st;
+  if ((st = check_device()) != FLP_OK) return st;
+  if (launch_embedding_forward(x_dtype, weight, ids, id_dtype == FLP_I64, N, D, V, out,
+                               static_cast<hipStream_t>(stream)) != hipSuccess)
+    return FLP_HIP_ERROR;
+  return FLP_OK;
+}
+
+size_t flp_embedding_backward_workspace_bytes(int64_t N, int64_t D, int64_t V) {
+  if (N < 0 || D < 1 || V < 1) return 0;
+  return emb_layout(N, D, V).total;
+}
+
+flp_status flp_embedding_backward(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
+                                  const void* grad, const void* ids, flp_dtype id_dtype,
+                                  void* d_weight, flp_dtype dw_dtype, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  flp_status st = validate_embedding_backward(N, D, V, x_dtype, grad, ids, id_dtype, d_weight,
+                                              dw_dtype, workspace, workspace_bytes);
+  if (st != FLP_OK || N == 0) return st;
+  if ((st = check_device()) != FLP_OK) return st;
+  const EmbLayout L = emb_layout(N, D, V);
+  EmbedBwdArgs a{};
+  a.x = x_dtype;
+  a.dw = dw_dtype;
+  a.grad = grad;
+  a.ids = ids;
+  a.i64 = id_dtype == FLP_I64;
+  a.N = N;
+  a.D = D;
+  a.V = V;
+  for (int k = 0; k < 2; ++k) {
+    a.keys[k] = reinterpret_cast<uint32_t*>(at(workspace, L.keys_off[k]));
+    a.vals[k] = reinterpret_cast<int32_t*>(at(workspace, L.vals_off[k]));
+  }
+  a.hist = reinterpret_cast<int32_t*>(at(workspace, L.hist_off));
+  a.seg_begin = reinterpret_cast<int32_t*>(at(workspace, L.seg_begin_off));
+  a.seg_end = reinterpret_cast<int32_t*>(at(workspace, L.seg_end_off));
+  a.head = reinterpret_cast<float*>(at(workspace, L.head_off));
+  a.tail = reinterpret_cast<float*>(at(workspace, L.tail_off));
+  a.d_weight = d_weight;
+  if (launch_embedding_backward(a, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return FLP_HIP_ERROR;
+  return FLP_OK;
+}
+
 void flp_profile_enable(int on) { g_prof_on.store(on != 0); }
 
 flp_status flp_profile_read(double* ms, int64_t* count, int n) {

@@ -1185,7 +1185,9 @@ const char* kernel_ids() {
          "BM 256 4x2 waves>; k_merge<8 rows x 32 segments>; k_dz<BM 256 x BN 256, 4x2 waves>; "
          "k_gemm dX, dW<256x224, 4x2 waves, K-blocked operands>; k_transpose (K-blocked); "
          "k_dbias_fold; k_fill; k_logits_fwd, k_logits_bwd<one wave per row>; "
-         "rows: k_mark, k_compact, k_gather, k_scatter_rows, k_scatter_hidden";
+         "rows: k_mark, k_compact, k_gather, k_scatter_rows, k_scatter_hidden; "
+         "embedding: k_embed_fwd, radix sort (k_sort_hist, k_scan_excl, k_sort_scatter), "
+         "k_seg_bounds, k_embed_bwd";
 }
 
 }  // namespace flp

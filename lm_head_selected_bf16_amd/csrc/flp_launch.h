@@ -110,6 +110,28 @@ hipError_t launch_scatter_rows(const int32_t* pos, int64_t N, const float* logp_
 hipError_t launch_scatter_hidden(const int32_t* pos, int64_t N, const void* dh_c, size_t row_bytes,
                                  void* dh, hipStream_t s);
 
+// Untied embedding lookup and its sorted-segment grad_weight (flp_embed.hip).
+struct EmbedBwdArgs {
+  flp_dtype x;               // dtype of grad (and of the embedding)
+  flp_dtype dw;              // x or FLP_F32
+  const void* grad;          // [N][D]
+  const void* ids;           // [N]
+  bool i64;
+  int64_t N, D, V;
+  uint32_t* keys[2];         // [N] radix-sort ping-pong buffers
+  int32_t* vals[2];          // [N]
+  int32_t* hist;             // [256][ceil(N / kEmbSortBlock)]
+  int32_t* seg_begin;        // [V]
+  int32_t* seg_end;          // [V]
+  float* head;               // [ceil(N / kEmbSegGroup)][D] fp32 pieces of segments that span groups
+  float* tail;               // same shape
+  void* d_weight;            // [V][D] dw
+};
+int embed_sort_passes(int64_t V);
+hipError_t launch_embedding_forward(flp_dtype x, const void* weight, const void* ids, bool i64,
+                                    int64_t N, int64_t D, int64_t V, void* out, hipStream_t s);
+hipError_t launch_embedding_backward(const EmbedBwdArgs& a, hipStream_t s);
+
 // Event brackets around each launch while profiling is enabled (flp_api.cpp).
 struct ProfScope {
   ProfScope(int kind, hipStream_t s);

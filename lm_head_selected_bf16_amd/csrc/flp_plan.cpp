@@ -170,6 +170,32 @@ IdxLayout idx_layout(int64_t N, int64_t D, int64_t n_rows, flp_dtype x, bool bac
   return L;
 }
 
+EmbLayout emb_layout(int64_t N, int64_t D, int64_t V) {
+  EmbLayout L;
+  const size_t n = size_t(std::max<int64_t>(N, 0));
+  L.n_blocks = ceil_div(std::max<int64_t>(N, 1), kEmbSortBlock);
+  size_t off = 0;
+  for (int k = 0; k < 2; ++k) {
+    L.keys_off[k] = off;
+    off += align_up(n * 4);
+    L.vals_off[k] = off;
+    off += align_up(n * 4);
+  }
+  L.hist_off = off;
+  off += align_up(size_t(256) * size_t(L.n_blocks) * 4);
+  L.seg_begin_off = off;
+  off += align_up(size_t(V) * 4);
+  L.seg_end_off = off;
+  off += align_up(size_t(V) * 4);
+  const size_t groups = size_t(ceil_div(std::max<int64_t>(N, 1), kEmbSegGroup));
+  L.head_off = off;
+  off += align_up(groups * size_t(D) * 4);
+  L.tail_off = off;
+  off += align_up(groups * size_t(D) * 4);
+  L.total = off;
+  return L;
+}
+
 flp_status validate_rows(int64_t N, const void* rows, flp_dtype r, int64_t n_rows) {
   if (N < 0 || n_rows < 0) return FLP_INVALID_ARGUMENT;
   if (r != FLP_I64 && r != FLP_I32) return FLP_UNSUPPORTED_DTYPE;
@@ -422,6 +448,59 @@ flp_status validate_logits_indexed(int64_t N, int64_t V, flp_dtype x, bool backw
                        span(workspace, workspace_bytes)};
   if (any_alias(outs, 3, ins, 5)) return FLP_INVALID_ARGUMENT;
   if (workspace_bytes < align_up(size_t(N))) return FLP_WORKSPACE_TOO_SMALL;
+  return FLP_OK;
+}
+
+namespace {
+
+flp_status check_embedding_dims(int64_t N, int64_t D, int64_t V, flp_dtype x, flp_dtype id) {
+  if (N < 0 || D < 1 || V < 1) return FLP_INVALID_ARGUMENT;
+  if (x != FLP_BF16 && x != FLP_F16 && x != FLP_F32) return FLP_UNSUPPORTED_DTYPE;
+  if (id != FLP_I64 && id != FLP_I32) return FLP_UNSUPPORTED_DTYPE;
+  // rows move in 16-byte chunks; token indices, sort keys (ids and the dropped-id
+  // key V) and segment bounds are 32-bit
+  if ((D * int64_t(dtype_size(x))) % 16 != 0) return FLP_UNSUPPORTED_SHAPE;
+  if (N > kMaxIndexedRows || V > kMaxIndexedRows - 1) return FLP_UNSUPPORTED_SHAPE;
+  if (!mul_ok(std::max<int64_t>(N, 1), D) || !mul_ok(V, D) || !mul_ok(V * D, 8))
+    return FLP_UNSUPPORTED_SHAPE;
+  return FLP_OK;
+}
+
+}  // namespace
+
+flp_status validate_embedding_forward(int64_t N, int64_t D, int64_t V, flp_dtype x,
+                                      const void* weight, const void* ids, flp_dtype id,
+                                      const void* out) {
+  flp_status st = check_embedding_dims(N, D, V, x, id);
+  if (st != FLP_OK || N == 0) return st;
+  if (!weight || !ids || !out) return FLP_INVALID_ARGUMENT;
+  if (!aligned(weight, 16) || !aligned(out, 16) || !aligned(ids, dtype_size(id)))
+    return FLP_MISALIGNED;
+  const size_t xs = dtype_size(x);
+  const Span ins[] = {span(weight, size_t(V) * D * xs), span(ids, size_t(N) * dtype_size(id))};
+  const Span outs[] = {span(out, size_t(N) * D * xs)};
+  if (any_alias(outs, 1, ins, 2)) return FLP_INVALID_ARGUMENT;
+  return FLP_OK;
+}
+
+flp_status validate_embedding_backward(int64_t N, int64_t D, int64_t V, flp_dtype x,
+                                       const void* grad, const void* ids, flp_dtype id,
+                                       const void* d_weight, flp_dtype dw, const void* workspace,
+                                       size_t workspace_bytes) {
+  flp_status st = check_embedding_dims(N, D, V, x, id);
+  if (st != FLP_OK) return st;
+  if (dw != x && dw != FLP_F32) return FLP_UNSUPPORTED_DTYPE;
+  if (N == 0) return FLP_OK;
+  if (!grad || !ids || !d_weight || !workspace) return FLP_INVALID_ARGUMENT;
+  if (!aligned(grad, 16) || !aligned(d_weight, 16) || !aligned(workspace, 16) ||
+      !aligned(ids, dtype_size(id)))
+    return FLP_MISALIGNED;
+  const size_t xs = dtype_size(x);
+  const Span ins[] = {span(grad, size_t(N) * D * xs), span(ids, size_t(N) * dtype_size(id))};
+  const Span outs[] = {span(d_weight, size_t(V) * D * dtype_size(dw)),
+                       span(workspace, workspace_bytes)};
+  if (any_alias(outs, 2, ins, 2)) return FLP_INVALID_ARGUMENT;
+  if (workspace_bytes < emb_layout(N, D, V).total) return FLP_WORKSPACE_TOO_SMALL;
   return FLP_OK;
 }
 

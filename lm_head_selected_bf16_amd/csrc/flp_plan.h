@@ -82,6 +82,17 @@ struct IdxLayout {
 IdxLayout idx_layout(int64_t N, int64_t D, int64_t n_rows, flp_dtype x, bool backward,
                      bool need_dh);
 
+// ---- embedding backward: radix-sort buffers and the per-id segments ----
+constexpr int64_t kEmbSortBlock = 256;  // keys per block of a radix pass
+constexpr int64_t kEmbSegGroup = 32;    // sorted positions per group of the segment sums
+struct EmbLayout {
+  int64_t n_blocks = 0;   // radix-sort blocks of kEmbSortBlock keys
+  size_t keys_off[2] = {0, 0}, vals_off[2] = {0, 0};
+  size_t hist_off = 0, seg_begin_off = 0, seg_end_off = 0;
+  size_t head_off = 0, tail_off = 0, total = 0;  // fp32 [ceil(N / kEmbSegGroup)][D] each
+};
+EmbLayout emb_layout(int64_t N, int64_t D, int64_t V);
+
 // ---- validation (pure host logic; never dereferences a pointer) ----
 flp_status validate_forward(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
                             const void* hidden, const void* weight, const float* bias,
@@ -138,5 +149,14 @@ flp_status validate_logits_indexed(int64_t N, int64_t V, flp_dtype x_dtype, bool
                                    flp_dtype r_dtype, int64_t n_rows, const void* out_a,
                                    const void* out_b, const void* workspace,
                                    size_t workspace_bytes);
+
+// Untied embedding lookup (forward) and its grad_weight (backward).
+flp_status validate_embedding_forward(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
+                                      const void* weight, const void* ids, flp_dtype id_dtype,
+                                      const void* out);
+flp_status validate_embedding_backward(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
+                                       const void* grad, const void* ids, flp_dtype id_dtype,
+                                       const void* d_weight, flp_dtype dw_dtype,
+                                       const void* workspace, size_t workspace_bytes);
 
 }  // namespace flp

@@ -453,3 +453,79 @@ class LogitsLogpIndexed(torch.autograd.Function):
 def logits_logp_indexed(logits, targets, rows):
     """logits_logp restricted to the rows listed in ``rows`` (full shape, zeros elsewhere)."""
     return LogitsLogpIndexed.apply(logits, targets, rows)
+
+
+# ---- untied embedding lookup -------------------------------------------------------------------
+#
+# out = weight[ids] (a zero row for ids outside [0, V)); d_weight sums the gradient rows of each
+# id in ascending token order in fp32 (PR #555 summary bullets: sorted-segment deterministic
+# grad_weight).
+
+def _prepare_embedding(weight, ids):
+    if weight.dtype not in _X_DTYPES:
+        raise TypeError("weight must be bfloat16, float16 or float32")
+    if ids.dtype not in _T_DTYPES:
+        raise TypeError("ids must be int64 or int32")
+    if not (weight.is_cuda and ids.is_cuda):
+        raise ValueError("weight and ids must be on the GPU")
+    if weight.dim() != 2 or not weight.is_contiguous() or not ids.is_contiguous():
+        raise ValueError("weight must be a contiguous [V, D] tensor and ids contiguous")
+    V, D = int(weight.shape[0]), int(weight.shape[1])
+    return V, D, ids.reshape(-1), int(ids.numel())
+
+
+def embedding_forward(weight: torch.Tensor, ids: torch.Tensor) -> torch.Tensor:
+    """weight[ids] with the ids' shape + [D], through flp_embedding_forward."""
+    V, D, i1, N = _prepare_embedding(weight, ids)
+    out = torch.empty(tuple(ids.shape) + (D,), dtype=weight.dtype, device=weight.device)
+    st = _abi.flp_embedding_forward(N, D, V, _X_DTYPES[weight.dtype], _ptr(weight), _ptr(i1),
+                                    _T_DTYPES[ids.dtype], _ptr(out), _stream(weight.device))
+    _check("flp_embedding_forward", st)
+    return out
+
+
+def embedding_backward(grad: torch.Tensor, ids: torch.Tensor, num_embeddings: int,
+                       dw_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
+    """d_weight [V, D] of sum(grad * weight[ids]) through flp_embedding_backward."""
+    if grad.dtype not in _X_DTYPES or not grad.is_contiguous() or not grad.is_cuda:
+        raise ValueError("grad must be a contiguous bfloat16 / float16 / float32 GPU tensor")
+    if ids.dtype not in _T_DTYPES or not ids.is_contiguous():
+        raise ValueError("ids must be contiguous int64 or int32")
+    D = int(grad.shape[-1])
+    if tuple(grad.shape[:-1]) != tuple(ids.shape):
+        raise ValueError("grad must have the ids' shape + [D]")
+    N, V = int(ids.numel()), int(num_embeddings)
+    dwt = grad.dtype if dw_dtype is None else dw_dtype
+    dev = grad.device
+    d_weight = torch.empty((V, D), dtype=dwt, device=dev)
+    if N == 0:
+        return d_weight.zero_()
+    ws = torch.empty(max(_abi.flp_embedding_backward_workspace_bytes(N, D, V), 16),
+                     dtype=torch.uint8, device=dev)
+    st = _abi.flp_embedding_backward(N, D, V, _X_DTYPES[grad.dtype], _ptr(grad), _ptr(ids),
+                                     _T_DTYPES[ids.dtype], _ptr(d_weight), _X_DTYPES[dwt],
+                                     _ptr(ws), ws.numel(), _stream(dev))
+    _check("flp_embedding_backward", st)
+    return d_weight
+
+
+class Embedding(torch.autograd.Function):
+    """Autograd node of the untied embedding lookup; the ids are not differentiable."""
+
+    @staticmethod
+    def forward(ctx, weight, ids):
+        ctx.save_for_backward(ids)
+        ctx.num_embeddings = int(weight.shape[0])
+        return embedding_forward(weight, ids)
+
+    @staticmethod
+    def backward(ctx, grad):
+        (ids,) = ctx.saved_tensors
+        if not ctx.needs_input_grad[0]:
+            return None, None
+        return embedding_backward(grad.contiguous(), ids, ctx.num_embeddings), None
+
+
+def embedding(weight, ids):
+    """weight[ids] (zero rows for ids outside [0, V)), differentiable in weight."""
+    return Embedding.apply(weight, ids)

@@ -69,6 +69,8 @@ __all__ = [
     "backward_indexed",
     "logits_forward_indexed",
     "logits_backward_indexed",
+    "embedding_forward",
+    "embedding_backward",
 ]
 
 
@@ -309,4 +311,34 @@ def logits_backward_indexed(logits_in, targets, grad_out, ids, chunk=512):
     out = np.zeros((N, V))
     if s.size:
         out[s] = logits_backward(logits_in, targets, grad_out, rows=s, chunk=chunk)
+    return out
+
+
+# ---- untied embedding lookup --------------------------------------------------------------------
+#
+# "Feat/nemotron h lm head logprob cuda" (PR #555), summary bullets: the untied
+# embedding lookup of the same model row, with a sorted-segment grad_weight.
+# The plain definitions: the lookup copies row ids[i] of the table; the
+# gradient of sum_i <grad_i, E[ids_i]> with respect to row v of E is the sum of
+# grad_i over the tokens with ids_i == v.  Reading adopted: an id outside
+# [0, V) reads as a zero row and contributes nothing (the path's convention for
+# out-of-range ids).
+
+def embedding_forward(weight, ids):
+    """[N, D] float64: row ids[i] of weight, a zero row for ids outside [0, V)."""
+    E = as_f64(weight)
+    i = _as_i64(ids).reshape(-1)
+    ok = (i >= 0) & (i < E.shape[0])
+    out = np.zeros((i.shape[0], E.shape[1]))
+    out[ok] = E[i[ok]]
+    return out
+
+
+def embedding_backward(grad, ids, num_embeddings):
+    """[V, D] float64: for each row v the sum of the gradient rows of the tokens with id v."""
+    G = as_f64(grad).reshape(-1, as_f64(grad).shape[-1])
+    i = _as_i64(ids).reshape(-1)
+    ok = (i >= 0) & (i < num_embeddings)
+    out = np.zeros((num_embeddings, G.shape[1]))
+    np.add.at(out, i[ok], G[ok])
     return out

@@ -410,4 +410,44 @@ def pin_logits_indexed_library(o):
     assert np.all(d[[1, 2, 4]] == 0.0)
 
 
+# ---- untied embedding lookup ------------------------------------------------------------------
+
+def pin_embedding_library(o):
+    """Lookup and its gradient against torch.nn.functional.embedding and autograd (valid ids),
+    and against the one-hot matrix form dE = onehot(ids)^T @ grad (a library matmul)."""
+    r = _rng(60)
+    V, D = 7, 5
+    E = r.standard_normal((V, D))
+    ids = np.array([3, 0, 3, 6, 3, 1, 0])
+    G = r.standard_normal((ids.size, D))
+    Et = torch.tensor(E, requires_grad=True)
+    out = torch.nn.functional.embedding(torch.tensor(ids), Et)
+    (out * torch.tensor(G)).sum().backward()
+    assert np.array_equal(o.embedding_forward(E, ids), out.detach().numpy())
+    dE = o.embedding_backward(G, ids, V)
+    assert np.max(np.abs(dE - Et.grad.numpy())) < 1e-13
+    onehot = (ids[:, None] == np.arange(V)[None, :]).astype(np.float64)
+    assert np.max(np.abs(dE - onehot.T @ G)) < 1e-13
+    assert not dE[[2, 4, 5]].any()  # ids that do not occur
+
+
+def pin_embedding_invalid_ids_and_permutation(o):
+    """Ids outside [0, V) read zero rows and add nothing; permuting tokens (ids and gradient
+    rows together) leaves the gradient unchanged; the rows of dE add up to the valid grads."""
+    r = _rng(61)
+    V, D = 6, 4
+    E = r.standard_normal((V, D))
+    ids = np.array([2, -1, 5, 6, 2, 0, -3, 2])
+    G = r.standard_normal((ids.size, D))
+    out = o.embedding_forward(E, ids)
+    ok = (ids >= 0) & (ids < V)
+    assert not out[~ok].any() and np.array_equal(out[ok], E[ids[ok]])
+    dE = o.embedding_backward(G, ids, V)
+    assert np.max(np.abs(dE - o.embedding_backward(G[ok], ids[ok], V))) < 1e-14
+    assert np.max(np.abs(dE.sum(axis=0) - G[ok].sum(axis=0))) < 1e-12
+    p = r.permutation(ids.size)
+    assert np.max(np.abs(o.embedding_backward(G[p], ids[p], V) - dE)) < 1e-12
+    assert np.max(np.abs(dE[2] - (G[0] + G[4] + G[7]))) < 1e-14
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -353,3 +353,62 @@ def libwd(**kw):
 ])
 def test_logits_backward_indexed_gates(kw, expect):
     assert abi.STATUS_NAMES[libwd(**kw)] == expect
+
+
+# ---- untied embedding lookup ----
+
+def efwd(**kw):
+    a = dict(N=N, D=64, V=V, x=BF16, w=W, ids=T, t=I64, out=0x90000000, stream=0)
+    a.update(kw)
+    return abi.flp_embedding_forward(a["N"], a["D"], a["V"], a["x"], a["w"], a["ids"], a["t"],
+                                     a["out"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(N=-1), "FLP_INVALID_ARGUMENT"),
+    (dict(V=0), "FLP_INVALID_ARGUMENT"),
+    (dict(x=I32), "FLP_UNSUPPORTED_DTYPE"),
+    (dict(t=F32), "FLP_UNSUPPORTED_DTYPE"),
+    (dict(D=4), "FLP_UNSUPPORTED_SHAPE"),               # rows move in 16-byte chunks
+    (dict(x=F32, D=6), "FLP_UNSUPPORTED_SHAPE"),
+    (dict(V=(1 << 31) - 1), "FLP_UNSUPPORTED_SHAPE"),   # id V must fit the 32-bit sort key
+    (dict(w=0), "FLP_INVALID_ARGUMENT"),
+    (dict(out=0x90000008), "FLP_MISALIGNED"),
+    (dict(ids=T + 4), "FLP_MISALIGNED"),
+    (dict(out=W + 64), "FLP_INVALID_ARGUMENT"),         # output inside the table
+    (dict(N=0, w=0, ids=0, out=0), "FLP_OK"),
+])
+def test_embedding_forward_gates(kw, expect):
+    assert abi.STATUS_NAMES[efwd(**kw)] == expect
+
+
+def ebwd(**kw):
+    a = dict(N=N, D=64, V=V, x=BF16, g=H, ids=T, t=I32, dw=0x90000000, dwt=BF16, ws=WS,
+             wsb=abi.flp_embedding_backward_workspace_bytes(N, 64, V), stream=0)
+    a.update(kw)
+    return abi.flp_embedding_backward(a["N"], a["D"], a["V"], a["x"], a["g"], a["ids"], a["t"],
+                                      a["dw"], a["dwt"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(dwt=I64), "FLP_UNSUPPORTED_DTYPE"),
+    (dict(x=F32, dwt=BF16), "FLP_UNSUPPORTED_DTYPE"),   # d_weight dtype must be x or f32
+    (dict(g=0), "FLP_INVALID_ARGUMENT"),
+    (dict(dw=0), "FLP_INVALID_ARGUMENT"),
+    (dict(ws=0), "FLP_INVALID_ARGUMENT"),
+    (dict(wsb=1024), "FLP_WORKSPACE_TOO_SMALL"),
+    (dict(dw=0x90000004), "FLP_MISALIGNED"),
+    (dict(dw=H), "FLP_INVALID_ARGUMENT"),               # d_weight overlaps grad
+    (dict(ws=0x90000000 + 1024), "FLP_INVALID_ARGUMENT"),  # workspace inside d_weight
+    (dict(N=0, g=0, ids=0, dw=0, ws=0), "FLP_OK"),
+])
+def test_embedding_backward_gates(kw, expect):
+    assert abi.STATUS_NAMES[ebwd(**kw)] == expect
+
+
+def test_embedding_workspace_bytes():
+    # two (key, value) sort buffers of N, the per-block digit counts, two [V] bounds, and
+    # two fp32 [N / 32, D] slots for segments that span groups
+    b = abi.flp_embedding_backward_workspace_bytes(16384, 2688, 131072)
+    assert b >= 4 * 16384 * 4 + 256 * 64 * 4 + 2 * 131072 * 4 + 2 * 512 * 2688 * 4
+    assert abi.flp_embedding_backward_workspace_bytes(-1, 64, 10) == 0

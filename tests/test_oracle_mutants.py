@@ -123,6 +123,20 @@ def _sel_off_by_one(n, ids):
     return np.unique(r[(r >= 0) & (r <= n)] % n)
 
 
+def _emb_bwd_drops_repeats(grad, ids, num_embeddings):
+    G = np.asarray(grad, dtype=np.float64)
+    i = np.asarray(ids, dtype=np.int64)
+    ok = (i >= 0) & (i < num_embeddings)
+    out = np.zeros((num_embeddings, G.shape[1]))
+    out[i[ok]] += G[ok]            # fancy-index += keeps one of the repeated ids
+    return out
+
+
+def _emb_fwd_wraps(weight, ids):
+    E = np.asarray(weight, dtype=np.float64)
+    return E[np.asarray(ids, dtype=np.int64) % E.shape[0]]
+
+
 MUTANTS = {
     "logits_no_bias": ("logits", _logits_no_bias),
     "logits_temp_multiplies": ("logits", _logits_temp_mul),
@@ -144,6 +158,8 @@ MUTANTS = {
     "selection_keeps_duplicate_ids": ("selected_rows", _sel_keeps_duplicates),
     "selection_wraps_negative_ids": ("selected_rows", _sel_wraps_negative),
     "selection_accepts_id_N": ("selected_rows", _sel_off_by_one),
+    "embedding_grad_drops_repeated_ids": ("embedding_backward", _emb_bwd_drops_repeats),
+    "embedding_lookup_wraps_ids": ("embedding_forward", _emb_fwd_wraps),
 }
 
 
