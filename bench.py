@@ -424,6 +424,23 @@ def embedding_op(N: int, D: int, V: int, steps: int, warmup: int):
     return res
 
 
+def fwd_bwd(name: str, steps: int, warmup: int):
+    """flp_forward + flp_backward on another workload (e.g. the 65600-token long sequence,
+    whose backward runs in row chunks with the fp32 d_W accumulator continued across them)."""
+    prob = Problem(name, backward=True)
+    ms, _, prof = prob.time_steps(steps, warmup)
+    N, D, V = prob.N, prob.D, prob.V
+    fl = 8.0 * N * D * V
+    out = {"workload": f"{name}: fwd+bwd, N={N}, D={D}, V={V}", "N": N, "steps": steps,
+           "ms_per_step": round(ms, 3), "tokens_per_s": round(N / (ms / 1e3), 1),
+           "method_TFLOPs": round(fl / (ms / 1e3) / 1e12, 1),
+           "method_frac_of_peak": round(fl / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "backward_chunks": int(prof["dlogits"][1] // max(steps, 1)),
+           "kernels_ms_per_step": {k: round(v[0] / steps, 3) for k, v in prof.items() if v[1]}}
+    del prob
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -526,6 +543,9 @@ def main() -> int:
         torch.cuda.empty_cache()
         log("untied embedding lookup: N=16384, D=2688, V=131072")
         out["embedding_n16384"] = embedding_op(16384, 2688, 131072, 10, 3)
+        torch.cuda.empty_cache()
+        log("long sequence: longseq_n65600 fwd+bwd")
+        out["longseq_n65600_fwd_bwd"] = fwd_bwd("longseq_n65600", 2, 1)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         cpu_prob = Problem.__new__(Problem)
