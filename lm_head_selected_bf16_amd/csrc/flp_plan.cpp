@@ -118,6 +118,23 @@ BwdLayout bwd_layout_for_bytes(int64_t N, int64_t D, int64_t V, flp_dtype x, flp
   int64_t nq = 0;
   if (per_quantum > 0 && bytes > fixed) nq = int64_t((bytes - fixed) / per_quantum);
   nq = std::min<int64_t>(nq, full / kRowQuantum);
+  if (need_dh && nq > 0) {
+    // Round the chunk down to a whole number of d_hidden waves when that is possible.
+    const bool f32 = x == FLP_F32;
+    const int64_t tm = f32 ? kGemmTile32 : kGemmTileM16, tn = f32 ? kGemmTile32 : kGemmTileN16;
+    const int64_t ct = ceil_div(D, tn);
+    int64_t a = ct, b = kNumCUs;  // gcd
+    while (b != 0) {
+      const int64_t r = a % b;
+      a = b;
+      b = r;
+    }
+    const int64_t wave_rows = (kNumCUs / a) * tm;
+    if (wave_rows % kRowQuantum == 0) {
+      const int64_t wq = wave_rows / kRowQuantum;
+      if (nq >= wq) nq = nq / wq * wq;
+    }
+  }
   for (; nq >= 1; --nq) {
     L = bwd_layout_for_chunk(N, D, V, x, dw, nq * kRowQuantum, need_dh, need_dw, need_db);
     if (L.total <= bytes) return L;

@@ -21,6 +21,13 @@ constexpr int64_t kRowQuantum = 256;
 constexpr int64_t kDzRowTile = 256;
 // K of the d_weight GEMM (tokens) is padded with zeros to a multiple of this.
 constexpr int64_t kTokPad = 64;
+// Output tiles of the backward GEMMs: 256 x 224 for 16-bit inputs, 128 x 128 for fp32.
+constexpr int64_t kGemmTileM16 = 256, kGemmTileN16 = 224, kGemmTile32 = 128;
+// Compute units of the targeted device (MI355X).  A backward that needs several
+// row chunks prefers chunks whose d_hidden GEMM fills whole waves of workgroups:
+// every d_hidden tile runs over all of K = V, so a nearly empty last wave costs
+// a full tile time.
+constexpr int64_t kNumCUs = 256;
 constexpr size_t kAlign = 256;
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
