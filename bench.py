@@ -128,18 +128,20 @@ class Problem:
         torch.cuda.synchronize()
         m.flp_profile_read()          # drop anything recorded before
         m.flp_profile_enable(True)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        e0.record()
-        for _ in range(steps):
+        ev[0].record()
+        for k in range(steps):
             self.step()
-        e1.record()
+            ev[k + 1].record()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         m.flp_profile_enable(False)
         prof = m.flp_profile_read()
-        return (t1 - t0) * 1e3 / steps, e0.elapsed_time(e1) / steps, prof
+        per = sorted(ev[k].elapsed_time(ev[k + 1]) for k in range(steps))
+        self.step_ms_median, self.step_ms_min = per[len(per) // 2], per[0]
+        return (t1 - t0) * 1e3 / steps, ev[0].elapsed_time(ev[steps]) / steps, prof
 
 
 def contraction_flops(kind: str, N: int, D: int, V: int, launches_per_step: int) -> float:
@@ -204,12 +206,14 @@ def forward_only(name: str, steps: int, warmup: int, bound: str):
         byts = prob.V * prob.D * 2 + prob.N * prob.D * 2 + prob.N * 8 + prob.N * 8
         out.update(bound="hbm", algorithmic_bytes=byts,
                    achieved_GBs=round(byts / (k_ms / 1e3) / 1e9, 1), peak_GBs=PEAK_HBM_GBS,
-                   frac=round(byts / (k_ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4))
+                   frac=round(byts / (k_ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+                   frac_of_measured_peak=_meas_frac("hbm", byts / (k_ms / 1e3) / 1e9))
     else:
         fl = 2.0 * prob.N * prob.D * prob.V
         out.update(bound="mfma", algorithmic_flops=fl,
                    achieved_TFLOPs=round(fl / (k_ms / 1e3) / 1e12, 1), peak_TFLOPs=PEAK_BF16_TFLOPS,
-                   frac=round(fl / (k_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4))
+                   frac=round(fl / (k_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                   frac_of_measured_peak=_meas_frac("mfma", fl / (k_ms / 1e3) / 1e12))
     del prob
     return out
 
@@ -252,12 +256,14 @@ def shard_forward(name: str, shards: int, steps: int, warmup: int, bound: str):
         byts = V_local * prob.D * 2 + prob.N * prob.D * 2 + prob.N * 8 + prob.N * 4
         out.update(bound="hbm", algorithmic_bytes=byts,
                    achieved_GBs=round(byts / (k_ms / 1e3) / 1e9, 1), peak_GBs=PEAK_HBM_GBS,
-                   frac=round(byts / (k_ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4))
+                   frac=round(byts / (k_ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+                   frac_of_measured_peak=_meas_frac("hbm", byts / (k_ms / 1e3) / 1e9))
     else:
         fl = 2.0 * prob.N * prob.D * V_local
         out.update(bound="mfma", algorithmic_flops=fl,
                    achieved_TFLOPs=round(fl / (k_ms / 1e3) / 1e12, 1), peak_TFLOPs=PEAK_BF16_TFLOPS,
-                   frac=round(fl / (k_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4))
+                   frac=round(fl / (k_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                   frac_of_measured_peak=_meas_frac("mfma", fl / (k_ms / 1e3) / 1e12))
     del prob
     return out
 
@@ -305,7 +311,8 @@ def logits_op(N: int, V: int, steps: int, warmup: int):
         gbs = byts / (k_ms / 1e3) / 1e9
         out[kind] = {"kernel_ms": round(k_ms, 4), "bound": "hbm", "algorithmic_bytes": byts,
                      "achieved_GBs": round(gbs, 1), "peak_GBs": PEAK_HBM_GBS,
-                     "frac": round(gbs / PEAK_HBM_GBS, 4)}
+                     "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "frac_of_measured_peak": _meas_frac("hbm", gbs)}
     del z, d
     return out
 
@@ -419,7 +426,8 @@ def embedding_op(N: int, D: int, V: int, steps: int, warmup: int):
         gbs = byts / (ms / 1e3) / 1e9
         res[kind] = {"ms": round(ms, 4), "bound": "hbm", "algorithmic_bytes": byts,
                      "achieved_GBs": round(gbs, 1), "peak_GBs": PEAK_HBM_GBS,
-                     "frac": round(gbs / PEAK_HBM_GBS, 4)}
+                     "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "frac_of_measured_peak": _meas_frac("hbm", gbs)}
     del w, g, out, dw, ws
     return res
 
@@ -438,6 +446,45 @@ def fwd_bwd(name: str, steps: int, warmup: int):
            "backward_chunks": int(prof["dlogits"][1] // max(steps, 1)),
            "kernels_ms_per_step": {k: round(v[0] / steps, 3) for k, v in prof.items() if v[1]}}
     del prob
+    return out
+
+
+_MEAS = {}  # filled by measured_peaks(): the probes' achievable rates
+
+
+def _meas_frac(bound: str, achieved: float):
+    key = "stream_read_GBs" if bound == "hbm" else "mfma_bf16_random_operands_TFLOPs"
+    return round(achieved / _MEAS[key], 4) if _MEAS.get(key) else None
+
+
+def measured_peaks():
+    """The chip's achievable rates from the library's probes: a dense bf16 MFMA loop on
+    random and on zero operands (with the shader clock it ran at) and a streaming read of
+    4 GiB."""
+    import torch
+
+    import lm_head_selected_bf16_amd as m
+
+    sb = m.flp_probe_scratch_bytes()
+    scratch = torch.empty(sb, dtype=torch.uint8, device="cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    out = {}
+    for name, zero in (("random", False), ("zero", True)):
+        st, tf, ghz = m.flp_probe_mfma(zero, 1000, scratch.data_ptr(), sb, stream)
+        if st != m.FLP_OK:
+            raise m.FlpError("flp_probe_mfma", st)
+        out[f"mfma_bf16_{name}_operands_TFLOPs"] = round(tf, 1)
+        out[f"clock_GHz_{name}_operands"] = round(ghz, 3)
+    buf = torch.empty(4 << 30, dtype=torch.uint8, device="cuda:0")
+    st, gbs = m.flp_probe_read(buf.data_ptr(), buf.numel(), scratch.data_ptr(), sb, stream)
+    if st != m.FLP_OK:
+        raise m.FlpError("flp_probe_read", st)
+    out["stream_read_GBs"] = round(gbs, 1)
+    _MEAS.update(out)
+    out["note"] = ("flp_probe_mfma: 2048 workgroups x 4 waves of v_mfma_f32_16x16x32_bf16 on "
+                   "register operands; flp_probe_read: 5 streaming passes over 4 GiB")
+    del buf
+    torch.cuda.empty_cache()
     return out
 
 
@@ -476,6 +523,9 @@ def main() -> int:
     torch.cuda.set_device(0)
     log(m.flp_build_info())
     name = "train_n16384"
+    log("measured peaks (probes)")
+    peaks = measured_peaks()
+    log(json.dumps(peaks))
     log(f"preparing {name}")
     prob = Problem(name, backward=True)
     N, D, V = prob.N, prob.D, prob.V
@@ -499,11 +549,13 @@ def main() -> int:
     dom_fl = contraction_flops(dom, N, D, V, dom_n)
     dom_avg_s = kernels[dom]["ms_per_launch"] / 1e3
     achieved = dom_fl / dom_avg_s / 1e12
+    meas = peaks["mfma_bf16_random_operands_TFLOPs"]
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": load_traffic(name, dom),
-                "algorithmic_flops_per_launch": dom_fl}
+                "algorithmic_flops_per_launch": dom_fl,
+                "measured_peak": meas, "frac_of_measured_peak": round(achieved / meas, 4)}
     step_flops = 8.0 * N * D * V
     value = N / (ms / 1e3)
     out = {
@@ -519,8 +571,12 @@ def main() -> int:
                                "with fp32 accumulation, single 16384-row backward chunk",
                    "N": N, "D": D, "V": V, "global_batch": 4, "seq_len": 4096,
                    "parallelism": "single GPU"},
+        "ms_per_step_median": round(prob.step_ms_median, 4),
+        "ms_per_step_min": round(prob.step_ms_min, 4),
         "method_TFLOPs": round(step_flops / (ms / 1e3) / 1e12, 1),
         "method_frac_of_peak": round(step_flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "method_frac_of_measured_peak": round(step_flops / (ms / 1e3) / 1e12 / meas, 4),
+        "measured_peaks": peaks,
         "roofline": roofline,
         "kernels": kernels,
     }

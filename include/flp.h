@@ -319,6 +319,32 @@ flp_status flp_embedding_backward(int64_t N, int64_t D, int64_t V, flp_dtype x_d
                                   size_t workspace_bytes, void* stream);
 
 /*
+ * Measurement probes (not part of the operator): the achievable dense bf16
+ * MFMA rate and the shader clock it runs at, and the achievable streaming-read
+ * bandwidth, so that figures can be quoted against measured peaks as well as
+ * nominal ones.  Unlike every other call these synchronise `stream` and return
+ * their results in host memory.
+ *
+ *   scratch        device buffer of >= flp_probe_scratch_bytes() bytes, 16-byte
+ *                  aligned; contents undefined afterwards.
+ *   flp_probe_mfma 2048 workgroups x 4 waves each run `iters` x 128
+ *                  v_mfma_f32_16x16x32_bf16 on register operands (random bf16
+ *                  values with |x| in [2^-7, 2), or zeros when zero_operands is
+ *                  nonzero), timed by HIP events after one untimed launch;
+ *                  *out_tflops = flops / time; *out_clock_ghz = median over
+ *                  workgroups of shader-clock cycles / real-time ticks during
+ *                  the loop x the real-time clock rate.  1 <= iters <= 10^6.
+ *   flp_probe_read reads `bytes` (a multiple of 16, 16-byte aligned) of
+ *                  `buffer` five times with streaming loads after one untimed
+ *                  pass; *out_gbs = bytes read / time.
+ */
+size_t flp_probe_scratch_bytes(void);
+flp_status flp_probe_mfma(int zero_operands, int64_t iters, void* scratch, size_t scratch_bytes,
+                          double* out_tflops, double* out_clock_ghz, void* stream);
+flp_status flp_probe_read(const void* buffer, size_t bytes, void* scratch, size_t scratch_bytes,
+                          double* out_gbs, void* stream);
+
+/*
  * Optional per-kernel timing with HIP events, for benchmarks.  While enabled,
  * every kernel the library enqueues is bracketed by two events recorded on
  * the same stream; flp_profile_read synchronises those events and returns, per

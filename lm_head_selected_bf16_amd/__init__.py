@@ -15,7 +15,8 @@ from ._abi import (FLP_BF16, FLP_F16, FLP_F32, FLP_I32, FLP_I64, FLP_OK, FlpErro
                    flp_forward_indexed_workspace_bytes, flp_forward_partial,
                    flp_forward_partial_bytes, flp_forward_workspace_bytes, flp_logits_backward,
                    flp_logits_backward_indexed, flp_logits_forward, flp_logits_forward_indexed,
-                   flp_logits_indexed_workspace_bytes, flp_merge, flp_profile_enable,
+                   flp_logits_indexed_workspace_bytes, flp_merge, flp_probe_mfma, flp_probe_read,
+                   flp_probe_scratch_bytes, flp_profile_enable,
                    flp_profile_read, flp_status_string, load)
 from .torch_ops import (LinearLogp, backward, backward_workspace_bytes,  # noqa: F401
                         LogitsLogp, default_backward_workspace_bytes, forward, forward_partial,
@@ -34,6 +35,7 @@ __all__ = [
     "flp_backward_indexed_workspace_bytes", "flp_logits_forward_indexed",
     "flp_logits_backward_indexed", "flp_logits_indexed_workspace_bytes",
     "flp_embedding_forward", "flp_embedding_backward", "flp_embedding_backward_workspace_bytes",
+    "flp_probe_scratch_bytes", "flp_probe_mfma", "flp_probe_read",
     "flp_status_string", "flp_build_info", "flp_profile_enable", "flp_profile_read", "load",
     "LinearLogp", "forward", "backward", "backward_workspace_bytes",
     "default_backward_workspace_bytes", "linear_logp", "linear_logp_with_lse",

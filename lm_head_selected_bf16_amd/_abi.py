@@ -57,6 +57,10 @@ SIGNATURES = {
     "flp_embedding_backward_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "flp_embedding_backward": (_int, [_i64, _i64, _i64, _int, _vp, _vp, _int, _vp, _int, _vp, _sz,
                                       _vp]),
+    "flp_probe_scratch_bytes": (_sz, []),
+    "flp_probe_mfma": (_int, [_int, _i64, _vp, _sz, ctypes.POINTER(ctypes.c_double),
+                              ctypes.POINTER(ctypes.c_double), _vp]),
+    "flp_probe_read": (_int, [_vp, _sz, _vp, _sz, ctypes.POINTER(ctypes.c_double), _vp]),
     "flp_profile_enable": (None, [_int]),
     "flp_profile_read": (_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64), _int]),
     "flp_status_string": (ctypes.c_char_p, [_int]),
@@ -220,6 +224,25 @@ def flp_embedding_backward(N, D, V, x_dtype, grad, ids, id_dtype, d_weight, dw_d
     """Raw call: every pointer argument is an int address (0 for NULL)."""
     return int(load().flp_embedding_backward(N, D, V, x_dtype, grad, ids, id_dtype, d_weight,
                                              dw_dtype, workspace, workspace_bytes, stream))
+
+
+def flp_probe_scratch_bytes() -> int:
+    return int(load().flp_probe_scratch_bytes())
+
+
+def flp_probe_mfma(zero_operands: bool, iters: int, scratch: int, scratch_bytes: int, stream: int):
+    """(status, TFLOP/s, shader clock GHz) of the dense MFMA probe (synchronises the stream)."""
+    tf, ghz = ctypes.c_double(0.0), ctypes.c_double(0.0)
+    st = int(load().flp_probe_mfma(int(bool(zero_operands)), iters, scratch, scratch_bytes,
+                                   ctypes.byref(tf), ctypes.byref(ghz), stream))
+    return st, tf.value, ghz.value
+
+
+def flp_probe_read(buffer: int, nbytes: int, scratch: int, scratch_bytes: int, stream: int):
+    """(status, GB/s) of the streaming-read probe (synchronises the stream)."""
+    gbs = ctypes.c_double(0.0)
+    st = int(load().flp_probe_read(buffer, nbytes, scratch, scratch_bytes, ctypes.byref(gbs), stream))
+    return st, gbs.value
 
 
 KERNEL_KINDS = ("forward", "merge", "dlogits", "transpose", "d_hidden", "d_weight", "d_bias",

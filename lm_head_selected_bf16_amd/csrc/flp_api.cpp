@@ -568,6 +568,39 @@ flp_status flp_embedding_backward(int64_t N, int64_t D, int64_t V, flp_dtype x_d
   return FLP_OK;
 }
 
+// ---- measurement probes ----
+
+size_t flp_probe_scratch_bytes(void) { return probe_scratch_bytes(); }
+
+flp_status flp_probe_mfma(int zero_operands, int64_t iters, void* scratch, size_t scratch_bytes,
+                          double* out_tflops, double* out_clock_ghz, void* stream) {
+  if (iters < 1 || iters > 1000000 || !scratch || !out_tflops || !out_clock_ghz)
+    return FLP_INVALID_ARGUMENT;
+  if (reinterpret_cast<uintptr_t>(scratch) % 16 != 0) return FLP_MISALIGNED;
+  if (scratch_bytes < probe_scratch_bytes()) return FLP_WORKSPACE_TOO_SMALL;
+  flp_status st = check_device();
+  if (st != FLP_OK) return st;
+  if (probe_mfma(zero_operands != 0 ? 1 : 0, iters, scratch, static_cast<hipStream_t>(stream),
+                 out_tflops, out_clock_ghz) != hipSuccess)
+    return FLP_HIP_ERROR;
+  return FLP_OK;
+}
+
+flp_status flp_probe_read(const void* buffer, size_t bytes, void* scratch, size_t scratch_bytes,
+                          double* out_gbs, void* stream) {
+  if (!buffer || bytes < 16 || bytes % 16 != 0 || !scratch || !out_gbs) return FLP_INVALID_ARGUMENT;
+  if (reinterpret_cast<uintptr_t>(buffer) % 16 != 0 || reinterpret_cast<uintptr_t>(scratch) % 16 != 0)
+    return FLP_MISALIGNED;
+  if (scratch_bytes < probe_scratch_bytes()) return FLP_WORKSPACE_TOO_SMALL;
+  const uintptr_t b0 = reinterpret_cast<uintptr_t>(buffer), s0 = reinterpret_cast<uintptr_t>(scratch);
+  if (b0 < s0 + scratch_bytes && s0 < b0 + bytes) return FLP_INVALID_ARGUMENT;
+  flp_status st = check_device();
+  if (st != FLP_OK) return st;
+  if (probe_read(buffer, bytes, scratch, static_cast<hipStream_t>(stream), out_gbs) != hipSuccess)
+    return FLP_HIP_ERROR;
+  return FLP_OK;
+}
+
 void flp_profile_enable(int on) { g_prof_on.store(on != 0); }
 
 flp_status flp_profile_read(double* ms, int64_t* count, int n) {

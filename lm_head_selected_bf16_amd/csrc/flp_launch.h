@@ -132,6 +132,12 @@ hipError_t launch_embedding_forward(flp_dtype x, const void* weight, const void*
                                     int64_t N, int64_t D, int64_t V, void* out, hipStream_t s);
 hipError_t launch_embedding_backward(const EmbedBwdArgs& a, hipStream_t s);
 
+// Measurement probes (flp_probe.hip); they synchronise the stream.
+size_t probe_scratch_bytes();
+hipError_t probe_mfma(int zero, int64_t iters, void* scratch, hipStream_t s, double* tflops,
+                      double* clock_ghz);
+hipError_t probe_read(const void* buf, size_t bytes, void* scratch, hipStream_t s, double* gbs);
+
 // Event brackets around each launch while profiling is enabled (flp_api.cpp).
 struct ProfScope {
   ProfScope(int kind, hipStream_t s);

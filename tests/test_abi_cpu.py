@@ -412,3 +412,35 @@ def test_embedding_workspace_bytes():
     b = abi.flp_embedding_backward_workspace_bytes(16384, 2688, 131072)
     assert b >= 4 * 16384 * 4 + 256 * 64 * 4 + 2 * 131072 * 4 + 2 * 512 * 2688 * 4
     assert abi.flp_embedding_backward_workspace_bytes(-1, 64, 10) == 0
+
+
+# ---- measurement probes (gates only: every case is rejected before the device is used) ----
+
+def test_probe_gates():
+    sb = abi.flp_probe_scratch_bytes()
+    assert sb >= 2048 * 4
+    bad = [
+        (dict(iters=0), "FLP_INVALID_ARGUMENT"),
+        (dict(iters=10 ** 7), "FLP_INVALID_ARGUMENT"),
+        (dict(scratch=0), "FLP_INVALID_ARGUMENT"),
+        (dict(scratch=WS + 8), "FLP_MISALIGNED"),
+        (dict(sbytes=sb - 1), "FLP_WORKSPACE_TOO_SMALL"),
+    ]
+    for kw, expect in bad:
+        a = dict(iters=10, scratch=WS, sbytes=sb)
+        a.update(kw)
+        st, _, _ = abi.flp_probe_mfma(False, a["iters"], a["scratch"], a["sbytes"], 0)
+        assert abi.STATUS_NAMES[st] == expect, kw
+    bad = [
+        (dict(buf=0), "FLP_INVALID_ARGUMENT"),
+        (dict(nbytes=8), "FLP_INVALID_ARGUMENT"),
+        (dict(nbytes=1000), "FLP_INVALID_ARGUMENT"),          # not a multiple of 16
+        (dict(buf=H + 4), "FLP_MISALIGNED"),
+        (dict(sbytes=16), "FLP_WORKSPACE_TOO_SMALL"),
+        (dict(buf=WS - 1024, nbytes=4096), "FLP_INVALID_ARGUMENT"),  # buffer overlaps scratch
+    ]
+    for kw, expect in bad:
+        a = dict(buf=H, nbytes=1 << 20, scratch=WS, sbytes=sb)
+        a.update(kw)
+        st, _ = abi.flp_probe_read(a["buf"], a["nbytes"], a["scratch"], a["sbytes"], 0)
+        assert abi.STATUS_NAMES[st] == expect, kw
