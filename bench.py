@@ -496,6 +496,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the forward-only decode (N=32) and rollout (N=8192) figures")
+    ap.add_argument("--only", choices=["decode_n32_forward", "rollout_n8192_forward"],
+                    help="run just this forward-only figure and print its JSON (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (reference for "
                          "the FETCH_SIZE / WRITE_SIZE counters)")
@@ -521,6 +523,11 @@ def main() -> int:
 
     m.load()
     torch.cuda.set_device(0)
+    if args.only:
+        wl, bound = {"decode_n32_forward": ("decode_n32", "hbm"),
+                     "rollout_n8192_forward": ("rollout_n8192", "mfma")}[args.only]
+        print(json.dumps({args.only: forward_only(wl, args.steps, args.warmup, bound)}), flush=True)
+        return 0
     log(m.flp_build_info())
     name = "train_n16384"
     log("measured peaks (probes)")
