@@ -79,20 +79,19 @@ __global__ __launch_bounds__(256) void k_probe_mfma(int64_t iters, int zero, flo
   }
 }
 
-// Streaming read: every thread sums 16-byte words with a grid stride; one value
-// per workgroup is written.
+// Streaming read: every thread xors 16-byte words with a grid stride, eight loads
+// in flight; one value per workgroup is written.
 __global__ __launch_bounds__(256) void k_probe_read(const u32x4* __restrict__ src, int64_t n,
                                                     uint32_t* __restrict__ out) {
   uint32_t x = 0;
   const int64_t stride = int64_t(gridDim.x) * 256;
   int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  for (; i + 3 * stride < n; i += 4 * stride) {  // four loads in flight
-    const u32x4 a = __builtin_nontemporal_load(src + i);
-    const u32x4 b = __builtin_nontemporal_load(src + i + stride);
-    const u32x4 c = __builtin_nontemporal_load(src + i + 2 * stride);
-    const u32x4 d = __builtin_nontemporal_load(src + i + 3 * stride);
-    x ^= (a[0] ^ a[1] ^ a[2] ^ a[3]) ^ (b[0] ^ b[1] ^ b[2] ^ b[3]) ^ (c[0] ^ c[1] ^ c[2] ^ c[3]) ^
-         (d[0] ^ d[1] ^ d[2] ^ d[3]);
+  for (; i + 7 * stride < n; i += 8 * stride) {
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x ^= (v[u][0] ^ v[u][1]) ^ (v[u][2] ^ v[u][3]);
   }
   for (; i < n; i += stride) {
     const u32x4 a = src[i];
@@ -146,7 +145,7 @@ hipError_t probe_mfma(int zero, int64_t iters, void* scratch, hipStream_t s, dou
 
 hipError_t probe_read(const void* buf, size_t bytes, void* scratch, hipStream_t s, double* gbs) {
   const int64_t n = int64_t(bytes / 16);
-  const unsigned grid = 256 * 16;
+  const unsigned grid = 256 * 8;
   hipEvent_t a = nullptr, b = nullptr;
   hipError_t e = hipEventCreate(&a);
   if (e == hipSuccess) e = hipEventCreate(&b);
