@@ -392,6 +392,9 @@ __global__ __launch_bounds__(128 * WM) void k_fwd(FwdArgs p) {
   Eng::template run<ODD>(acc, reinterpret_cast<const char*>(p.hidden) + row0 * kbytes, kbytes, p.N - row0,
            reinterpret_cast<const char*>(p.weight) + col0 * kbytes, kbytes, p.V - col0, kbytes,
            smem);
+  // Waves still reading their last fragments after the last stage barrier may read
+  // either buffer (buffer 0 when the stage count is odd): LDS is reused below.
+  __syncthreads();
 
   float* red = reinterpret_cast<float*>(smem);  // [2][BM] row max, then [2][BM] row sums
   const int64_t cw = col0 + wn * kHalfCols;
