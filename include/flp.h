@@ -25,8 +25,9 @@
  *     kernel timing below is enabled, a pool of HIP events); the calls are
  *     re-entrant.
  *   - Work is enqueued on `stream` (a hipStream_t, or NULL for the default
- *     stream) and the call returns at once.  Outputs are valid once the
- *     stream has synchronised; device faults surface there.
+ *     stream) and the call returns at once (the measurement probes at the end
+ *     are the one exception).  Outputs are valid once the stream has
+ *     synchronised; device faults surface there.
  *   - Inputs are read-only.  Outputs are overwritten, never accumulated.
  *     No output may overlap any input or another output (checked from the
  *     address ranges; FLP_INVALID_ARGUMENT otherwise).
