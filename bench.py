@@ -193,12 +193,50 @@ def cpu_baseline(prob: Problem, target_s: float = 15.0):
             "host_cpus": os.cpu_count(), "affinity": len(os.sched_getaffinity(0))}
 
 
+def cpu_oracle_configs():
+    """The oracle's full runs on the small configurations: the fp32 tiny fwd+bwd and the
+    decode forward (N = 32 rows of the full vocabulary)."""
+    import threadpoolctl
+
+    import flp_inputs
+    import oracle
+
+    info = [i for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    out = {"cores": int(threads), "kind": "oracle"}
+    inp = flp_inputs.make_inputs("tiny_fp32")
+    t0 = time.perf_counter()
+    oracle.forward(inp["hidden"], inp["weight"], inp["targets"], inp["bias"], inp["temperature"])
+    oracle.backward(inp["hidden"], inp["weight"], inp["targets"], inp["grad_out"], inp["bias"],
+                    inp["temperature"])
+    dt = time.perf_counter() - t0
+    out["tiny_fp32_fwd_bwd"] = {"seconds": round(dt, 3), "tokens_per_s": round(64 / dt, 1)}
+    inp = flp_inputs.make_inputs("decode_n32")
+    t0 = time.perf_counter()
+    oracle.forward(inp["hidden"], inp["weight"], inp["targets"], inp["bias"], inp["temperature"])
+    dt = time.perf_counter() - t0
+    out["decode_n32_fwd"] = {"seconds": round(dt, 3), "tokens_per_s": round(32 / dt, 1)}
+    return out
+
+
 def forward_only(name: str, steps: int, warmup: int, bound: str):
+    import torch
+
     prob = Problem(name, backward=False)
+    # the first call of this process on this workload, before any warm-up
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    prob.forward()
+    e1.record()
+    torch.cuda.synchronize()
+    first_ms = e0.elapsed_time(e1)
     ms, ems, prof = prob.time_steps(steps, warmup)
     fwd_ms, fwd_n = prof["forward"]
     k_ms = fwd_ms / max(fwd_n, 1)
     out = {"workload": name, "N": prob.N, "ms_per_call": round(ms, 4),
+           "ms_per_call_median": round(prob.step_ms_median, 4),
+           "ms_per_call_min": round(prob.step_ms_min, 4), "first_call_ms": round(first_ms, 4),
            "tokens_per_s": round(prob.N / (ms / 1e3), 1), "forward_kernel_ms": round(k_ms, 4),
            "merge_kernel_ms": round(prof["merge"][0] / max(prof["merge"][1], 1), 4)}
     if bound == "hbm":
@@ -617,6 +655,7 @@ def main() -> int:
         cpu_prob.w = cpu_prob.cpu["workload"]
         cpu_prob.N, cpu_prob.D, cpu_prob.V = cpu_prob.w.N, cpu_prob.w.D, cpu_prob.w.V
         out["cpu_baseline"] = cpu_baseline(cpu_prob)
+        out["cpu_oracle_configs"] = cpu_oracle_configs()
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
