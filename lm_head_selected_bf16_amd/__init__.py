@@ -6,6 +6,13 @@ and its backward to hidden, W and b, computed by hand-written HIP kernels in
 libflp.so behind the C ABI of include/flp.h.  This package holds the build
 script, the ctypes binding (same names as the C ABI) and a thin PyTorch
 wrapper with autograd.
+
+Also behind the same ABI: the vocabulary-shard partial forward and its merge
+(forward_partial, merge), the operator on materialised logits (logits_logp,
+logits_forward, logits_backward), the indexed row-subset variants of both
+operators (linear_logp_indexed, logits_logp_indexed, ...), the untied embedding
+lookup with its deterministic grad_weight (embedding), and measurement probes
+(flp_probe_mfma, flp_probe_read).
 """
 from ._abi import (FLP_BF16, FLP_F16, FLP_F32, FLP_I32, FLP_I64, FLP_OK, FlpError,  # noqa: F401
                    flp_backward, flp_backward_indexed, flp_backward_indexed_workspace_bytes,
