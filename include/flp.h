@@ -187,13 +187,24 @@ flp_status flp_logits_backward(int64_t N, int64_t V, flp_dtype x_dtype, const fl
 
 /*
  * Backward workspace in bytes.  chunk_rows = 0 asks for the minimum (row
- * chunks of 256); a positive chunk_rows asks for the size that lets the
+ * chunks of 256, or one chunk of the whole batch when that needs less because a
+ * single chunk needs no fp32 d_W accumulator); a positive chunk_rows asks for the size that lets the
  * backward process that many rows per chunk (rounded up to a multiple of
  * 256, capped at N rounded up).  Any workspace at least the minimum is
  * accepted; a larger one gives larger chunks and the same bits.
  */
 size_t flp_backward_workspace_bytes(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
                                     flp_dtype dw_dtype, int64_t chunk_rows);
+
+/*
+ * Rows per chunk that flp_backward uses with `workspace_bytes` of workspace
+ * when the outputs flagged by need_* (0 or 1) are requested: a multiple of 256,
+ * at most N rounded up to 256, or 0 when the workspace is below the minimum.
+ * Pure host arithmetic (no device needed); the chunking never changes the bits.
+ */
+int64_t flp_backward_chunk_rows(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
+                                flp_dtype dw_dtype, size_t workspace_bytes, int need_d_hidden,
+                                int need_d_weight, int need_d_bias);
 
 /*
  * Backward of L = sum_i grad_out[i] * logp[i]:

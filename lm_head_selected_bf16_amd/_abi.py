@@ -40,6 +40,7 @@ SIGNATURES = {
     "flp_logits_forward": (_int, [_i64, _i64, _int, _vp, _vp, _int, _fp, _fp, _vp]),
     "flp_logits_backward": (_int, [_i64, _i64, _int, _fp, _fp, _vp, _vp, _int, _vp, _vp]),
     "flp_backward_workspace_bytes": (_sz, [_i64, _i64, _i64, _int, _int, _i64]),
+    "flp_backward_chunk_rows": (_i64, [_i64, _i64, _i64, _int, _int, _sz, _int, _int, _int]),
     "flp_backward": (_int, [_i64, _i64, _i64, _int, _fp, _fp, _vp, _vp, _fp, _vp, _int, _fp, _vp,
                             _vp, _int, _fp, _vp, _sz, _vp]),
     "flp_forward_indexed_workspace_bytes": (_sz, [_i64, _i64, _i64, _int, _i64]),
@@ -142,6 +143,14 @@ def flp_logits_backward(N, V, x_dtype, grad_out, lse, logits, targets, t_dtype, 
 def flp_backward_workspace_bytes(N: int, D: int, V: int, x_dtype: int, dw_dtype: int,
                                  chunk_rows: int = 0) -> int:
     return int(load().flp_backward_workspace_bytes(N, D, V, x_dtype, dw_dtype, chunk_rows))
+
+
+def flp_backward_chunk_rows(N: int, D: int, V: int, x_dtype: int, dw_dtype: int,
+                            workspace_bytes: int, need_d_hidden: bool = True,
+                            need_d_weight: bool = True, need_d_bias: bool = True) -> int:
+    return int(load().flp_backward_chunk_rows(N, D, V, x_dtype, dw_dtype, workspace_bytes,
+                                              int(need_d_hidden), int(need_d_weight),
+                                              int(need_d_bias)))
 
 
 def flp_forward(N, D, V, x_dtype, hidden, weight, bias, targets, t_dtype, temperature,

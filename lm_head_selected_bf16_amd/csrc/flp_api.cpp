@@ -228,8 +228,25 @@ size_t flp_backward_workspace_bytes(int64_t N, int64_t D, int64_t V, flp_dtype x
   if (N < 0 || D < 1 || V < 1 || chunk_rows < 0) return 0;
   if (x_dtype != FLP_BF16 && x_dtype != FLP_F16 && x_dtype != FLP_F32) return 0;
   if (N == 0) return 0;
-  const int64_t chunk = chunk_rows == 0 ? kRowQuantum : chunk_rows;
-  return bwd_layout_for_chunk(N, D, V, x_dtype, dw_dtype, chunk, true, true, true).total;
+  if (chunk_rows > 0)
+    return bwd_layout_for_chunk(N, D, V, x_dtype, dw_dtype, chunk_rows, true, true, true).total;
+  // The minimum: 256-row chunks, or one chunk of the whole batch when that is smaller
+  // (a single chunk needs no fp32 d_W accumulator, which can outweigh its larger buffers).
+  const size_t q = bwd_layout_for_chunk(N, D, V, x_dtype, dw_dtype, kRowQuantum, true, true, true).total;
+  const size_t one = bwd_layout_for_chunk(N, D, V, x_dtype, dw_dtype, N, true, true, true).total;
+  return q < one ? q : one;
+}
+
+int64_t flp_backward_chunk_rows(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
+                                flp_dtype dw_dtype, size_t workspace_bytes, int need_d_hidden,
+                                int need_d_weight, int need_d_bias) {
+  if (N < 1 || D < 1 || V < 1) return 0;
+  if (x_dtype != FLP_BF16 && x_dtype != FLP_F16 && x_dtype != FLP_F32) return 0;
+  if (dw_dtype != x_dtype && dw_dtype != FLP_F32) return 0;
+  if (!need_d_hidden && !need_d_weight && !need_d_bias) return 0;
+  return bwd_layout_for_bytes(N, D, V, x_dtype, dw_dtype, workspace_bytes, need_d_hidden != 0,
+                              need_d_weight != 0, need_d_bias != 0)
+      .chunk;
 }
 
 flp_status flp_backward(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,

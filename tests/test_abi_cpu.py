@@ -444,3 +444,52 @@ def test_probe_gates():
         a.update(kw)
         st, _ = abi.flp_probe_read(a["buf"], a["nbytes"], a["scratch"], a["sbytes"], 0)
         assert abi.STATUS_NAMES[st] == expect, kw
+
+
+# ---- the backward's chunk planner (pure host arithmetic) ----
+
+from hypothesis import given, settings, strategies as st  # noqa: E402
+
+_DT = [(BF16, BF16), (BF16, F32), (F32, F32), (abi.FLP_F16, abi.FLP_F16)]
+
+
+@settings(max_examples=300, deadline=None)
+@given(N=st.integers(1, 200000), D=st.integers(1, 160).map(lambda k: 32 * k),
+       V=st.integers(1, 300000), dt=st.sampled_from(_DT), chunk=st.integers(0, 70000),
+       needs=st.sampled_from([(1, 1, 1), (1, 0, 0), (0, 1, 0), (0, 0, 1), (1, 1, 0)]))
+def test_chunk_planner_properties(N, D, V, dt, chunk, needs):
+    """The workspace asked for a chunk size is accepted and yields at least that chunk
+    (capped at N rounded up to 256); the minimum yields a chunk; a chunk is a multiple of
+    256; one byte less than the minimum yields none; more bytes never give a smaller chunk."""
+    x, dw = dt
+    q = 256
+    full = -(-N // q) * q
+    lo = abi.flp_backward_workspace_bytes(N, D, V, x, dw, 0)
+    c_lo = abi.flp_backward_chunk_rows(N, D, V, x, dw, lo, *needs)
+    assert c_lo >= q and c_lo % q == 0 and c_lo <= full
+    if all(needs):
+        assert abi.flp_backward_chunk_rows(N, D, V, x, dw, lo - 1, *needs) == 0
+    want = min(-(-max(chunk, 1) // q) * q, full)
+    b = abi.flp_backward_workspace_bytes(N, D, V, x, dw, max(chunk, 1))
+    c = abi.flp_backward_chunk_rows(N, D, V, x, dw, b, *needs)
+    assert c >= q and c % q == 0 and c <= full
+    if all(needs) and want == full:
+        assert c == full  # a workspace sized for the whole batch runs it as one chunk
+    assert abi.flp_backward_chunk_rows(N, D, V, x, dw, b + (1 << 30), *needs) >= c
+
+
+def test_chunk_planner_examples():
+    # the long sequence in 16 GiB: chunks of 16384 rows (whole d_hidden waves)
+    assert abi.flp_backward_chunk_rows(65600, 2688, 131072, BF16, BF16, 16 << 30) == 16384
+    # the training batch in one chunk when it fits
+    one = abi.flp_backward_workspace_bytes(16384, 2688, 131072, BF16, BF16, 16384)
+    assert abi.flp_backward_chunk_rows(16384, 2688, 131072, BF16, BF16, one) == 16384
+    # the minimum for 630 rows (accepted exactly; once rejected by an off-by-slack search)
+    lo = abi.flp_backward_workspace_bytes(630, 128, 1000, BF16, BF16, 0)
+    assert abi.flp_backward_chunk_rows(630, 128, 1000, BF16, BF16, lo) == 256
+    assert abi.flp_backward_chunk_rows(0, 128, 1000, BF16, BF16, lo) == 0
+    # a small vocabulary: one 512-row chunk (no fp32 accumulator) needs less than two of 256
+    lo = abi.flp_backward_workspace_bytes(257, 1344, 177, BF16, BF16, 0)
+    assert lo == abi.flp_backward_workspace_bytes(257, 1344, 177, BF16, BF16, 512)
+    assert abi.flp_backward_chunk_rows(257, 1344, 177, BF16, BF16, lo) == 512
+    assert abi.flp_backward_chunk_rows(257, 1344, 177, BF16, BF16, lo - 1) == 0
