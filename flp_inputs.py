@@ -165,7 +165,7 @@ def make_embedding_inputs(N: int, D: int, V: int, dtype: torch.dtype, seed: int,
     `dtype`.  ids = "zipf": a heavy-headed token-frequency draw, floor(V^u) - 1 for u
     uniform (many repeats of the frequent ids, most ids absent); "uniform": uniform over
     [0, V); "same": every token has id V // 2.  The given out-of-range values replace
-    the first len(invalid) ids."""
+    the first ids (as many as there are tokens)."""
     g = torch.Generator(device=device)
     g.manual_seed(1000 * seed)
     E = torch.empty(V, D, dtype=torch.float32, device=device).normal_(0.0, 0.02, generator=g)
@@ -178,8 +178,9 @@ def make_embedding_inputs(N: int, D: int, V: int, dtype: torch.dtype, seed: int,
         t = torch.randint(0, V, (N,), generator=gc)
     else:
         t = torch.full((N,), V // 2, dtype=torch.int64)
-    if invalid:
-        t[:len(invalid)] = torch.tensor(invalid, dtype=torch.int64)
+    k = min(len(invalid), N)
+    if k:
+        t[:k] = torch.tensor(invalid[:k], dtype=torch.int64)
     grad = torch.empty(N, D, dtype=torch.float32, device=device).normal_(0.0, 1.0, generator=g)
     return dict(weight=E.to(dtype), ids=t, grad=grad.to(dtype))
 
