@@ -34,7 +34,9 @@
  *   - Every argument is validated before anything is enqueued.  On any
  *     non-OK status nothing has been enqueued and no output was touched.
  *     There is no fallback path: an unsupported case is an error.
- *   - N = 0 returns FLP_OK and enqueues nothing.
+ *   - N = 0 enqueues nothing, except that the backward calls still write
+ *     d_weight and d_bias (when given) as zeros: they are sums over the
+ *     rows, and a sum over no rows is zero.
  *   - Results are deterministic and batch-invariant: logp, lse and each row
  *     of d_hidden are bitwise the same whatever the other rows are, whatever
  *     N is and wherever the row sits; d_weight and d_bias are bitwise the

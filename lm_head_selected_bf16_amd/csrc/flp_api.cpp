@@ -35,6 +35,16 @@ flp_status check_device() {
 
 inline char* at(void* base, size_t off) { return static_cast<char*>(base) + off; }
 
+// The sums over the rows of an empty batch (or an empty selection) are zero.
+flp_status zero_sums(void* d_weight, size_t dw_bytes, float* d_bias, int64_t V, hipStream_t s) {
+  if (d_weight == nullptr && d_bias == nullptr) return FLP_OK;
+  const flp_status st = check_device();
+  if (st != FLP_OK) return st;
+  if (d_weight != nullptr && launch_zero(d_weight, dw_bytes, s) != hipSuccess) return FLP_HIP_ERROR;
+  if (d_bias != nullptr && launch_zero(d_bias, size_t(V) * 4, s) != hipSuccess) return FLP_HIP_ERROR;
+  return FLP_OK;
+}
+
 // ---- optional per-kernel event timing ----
 struct ProfRec {
   int kind;
@@ -258,10 +268,11 @@ flp_status flp_backward(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
   flp_status st = validate_backward(N, D, V, x_dtype, grad_out, lse, hidden, weight, bias, targets,
                                     t_dtype, temperature, d_hidden, d_weight, dw_dtype, d_bias,
                                     workspace, workspace_bytes);
-  if (st != FLP_OK || N == 0) return st;
+  if (st != FLP_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (N == 0) return zero_sums(d_weight, size_t(V) * D * dtype_size(dw_dtype), d_bias, V, s);
   if (!d_hidden && !d_weight && !d_bias) return FLP_OK;
   if ((st = check_device()) != FLP_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   const BwdLayout L = bwd_layout_for_bytes(N, D, V, x_dtype, dw_dtype, workspace_bytes,
                                            d_hidden != nullptr, d_weight != nullptr,
                                            d_bias != nullptr);
@@ -427,10 +438,12 @@ flp_status flp_backward_indexed(int64_t N, int64_t D, int64_t V, flp_dtype x_dty
                                             targets, t_dtype, temperature, rows, r_dtype, n_rows,
                                             d_hidden, d_weight, dw_dtype, d_bias, workspace,
                                             workspace_bytes);
-  if (st != FLP_OK || N == 0) return st;
+  if (st != FLP_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t dw_bytes = size_t(V) * D * dtype_size(dw_dtype);
+  if (N == 0) return zero_sums(d_weight, dw_bytes, d_bias, V, s);
   if (!d_hidden && !d_weight && !d_bias) return FLP_OK;
   if ((st = check_device()) != FLP_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   const IdxLayout L = idx_layout(N, D, n_rows, x_dtype, true, d_hidden != nullptr);
   const int64_t cap = L.sel.cap;
   const size_t row_bytes = size_t(D) * dtype_size(x_dtype);
@@ -460,11 +473,8 @@ flp_status flp_backward_indexed(int64_t N, int64_t D, int64_t V, flp_dtype x_dty
                       g.temp_c, dh_c, d_weight, dw_dtype, d_bias, at(workspace, L.dense_off),
                       workspace_bytes - L.dense_off, stream);
     if (st != FLP_OK) return st;
-  } else {
-    // Nothing can be selected: the sums over the selected rows are empty.
-    if (d_weight && launch_zero(d_weight, size_t(V) * D * dtype_size(dw_dtype), s) != hipSuccess)
-      return FLP_HIP_ERROR;
-    if (d_bias && launch_zero(d_bias, size_t(V) * 4, s) != hipSuccess) return FLP_HIP_ERROR;
+  } else if ((st = zero_sums(d_weight, dw_bytes, d_bias, V, s)) != FLP_OK) {
+    return st;  // nothing can be selected
   }
   if (d_hidden && launch_scatter_hidden(pos, N, dh_c, row_bytes, d_hidden, s) != hipSuccess)
     return FLP_HIP_ERROR;
@@ -558,7 +568,10 @@ flp_status flp_embedding_backward(int64_t N, int64_t D, int64_t V, flp_dtype x_d
                                   size_t workspace_bytes, void* stream) {
   flp_status st = validate_embedding_backward(N, D, V, x_dtype, grad, ids, id_dtype, d_weight,
                                               dw_dtype, workspace, workspace_bytes);
-  if (st != FLP_OK || N == 0) return st;
+  if (st != FLP_OK) return st;
+  if (N == 0)
+    return zero_sums(d_weight, size_t(V) * D * dtype_size(dw_dtype), nullptr, V,
+                     static_cast<hipStream_t>(stream));
   if ((st = check_device()) != FLP_OK) return st;
   const EmbLayout L = emb_layout(N, D, V);
   EmbedBwdArgs a{};

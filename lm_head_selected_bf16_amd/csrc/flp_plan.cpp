@@ -46,6 +46,16 @@ bool any_alias(const Span* outs, int n_out, const Span* ins, int n_in) {
   return false;
 }
 
+// An empty batch writes only d_weight and d_bias, as zeros (sums over no rows).
+flp_status validate_empty_sums(int64_t D, int64_t V, size_t xs, const void* weight,
+                               const float* bias, const void* d_weight, flp_dtype dw,
+                               const float* d_bias) {
+  if (!aligned(d_weight, 16) || !aligned(d_bias, 4)) return FLP_MISALIGNED;
+  const Span ins[] = {span(weight, size_t(V) * D * xs), span(bias, size_t(V) * 4)};
+  const Span outs[] = {span(d_weight, size_t(V) * D * dtype_size(dw)), span(d_bias, size_t(V) * 4)};
+  return any_alias(outs, 2, ins, 2) ? FLP_INVALID_ARGUMENT : FLP_OK;
+}
+
 flp_status check_dims(int64_t N, int64_t D, int64_t V, flp_dtype x, flp_dtype t) {
   if (N < 0 || D < 1 || V < 1) return FLP_INVALID_ARGUMENT;
   if (x != FLP_BF16 && x != FLP_F16 && x != FLP_F32) return FLP_UNSUPPORTED_DTYPE;
@@ -351,7 +361,7 @@ flp_status validate_backward(int64_t N, int64_t D, int64_t V, flp_dtype x, const
   flp_status st = check_dims(N, D, V, x, t);
   if (st != FLP_OK) return st;
   if (dw != x && dw != FLP_F32) return FLP_UNSUPPORTED_DTYPE;
-  if (N == 0) return FLP_OK;
+  if (N == 0) return validate_empty_sums(D, V, dtype_size(x), weight, bias, d_weight, dw, d_bias);
   if (!grad_out || !lse || !hidden || !weight || !targets) return FLP_INVALID_ARGUMENT;
   if (!d_hidden && !d_weight && !d_bias) return FLP_OK;
   if (!workspace) return FLP_INVALID_ARGUMENT;
@@ -414,7 +424,7 @@ flp_status validate_backward_indexed(int64_t N, int64_t D, int64_t V, flp_dtype 
   if (st != FLP_OK) return st;
   if (dw != x && dw != FLP_F32) return FLP_UNSUPPORTED_DTYPE;
   if ((st = validate_rows(N, rows, r, n_rows)) != FLP_OK) return st;
-  if (N == 0) return FLP_OK;
+  if (N == 0) return validate_empty_sums(D, V, dtype_size(x), weight, bias, d_weight, dw, d_bias);
   if (!grad_out || !lse || !hidden || !weight || !targets) return FLP_INVALID_ARGUMENT;
   if (!d_hidden && !d_weight && !d_bias) return FLP_OK;
   if (!workspace) return FLP_INVALID_ARGUMENT;
@@ -507,8 +517,9 @@ flp_status validate_embedding_backward(int64_t N, int64_t D, int64_t V, flp_dtyp
   flp_status st = check_embedding_dims(N, D, V, x, id);
   if (st != FLP_OK) return st;
   if (dw != x && dw != FLP_F32) return FLP_UNSUPPORTED_DTYPE;
-  if (N == 0) return FLP_OK;
-  if (!grad || !ids || !d_weight || !workspace) return FLP_INVALID_ARGUMENT;
+  if (!d_weight) return FLP_INVALID_ARGUMENT;
+  if (N == 0) return validate_empty_sums(D, V, dtype_size(x), nullptr, nullptr, d_weight, dw, nullptr);
+  if (!grad || !ids || !workspace) return FLP_INVALID_ARGUMENT;
   if (!aligned(grad, 16) || !aligned(d_weight, 16) || !aligned(workspace, 16) ||
       !aligned(ids, dtype_size(id)))
     return FLP_MISALIGNED;

@@ -498,8 +498,6 @@ def embedding_backward(grad: torch.Tensor, ids: torch.Tensor, num_embeddings: in
     dwt = grad.dtype if dw_dtype is None else dw_dtype
     dev = grad.device
     d_weight = torch.empty((V, D), dtype=dwt, device=dev)
-    if N == 0:
-        return d_weight.zero_()
     ws = torch.empty(max(_abi.flp_embedding_backward_workspace_bytes(N, D, V), 16),
                      dtype=torch.uint8, device=dev)
     st = _abi.flp_embedding_backward(N, D, V, _X_DTYPES[grad.dtype], _ptr(grad), _ptr(ids),

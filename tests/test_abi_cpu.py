@@ -163,7 +163,12 @@ def bwd(**kw):
     (dict(db=0xA0000000 + 64), "FLP_INVALID_ARGUMENT"), # d_bias inside d_weight
     (dict(wsb=1000), "FLP_WORKSPACE_TOO_SMALL"),
     (dict(dh=0, dw=0, db=0, ws=0), "FLP_OK"),           # nothing requested: no-op
-    (dict(N=0, g=0, lse=0, hidden=0, targets=0, ws=0), "FLP_OK"),
+    # empty batch: only d_weight / d_bias would be written (zeros), so they are checked
+    (dict(N=0, g=0, lse=0, hidden=0, targets=0, ws=0, dw=0, db=0), "FLP_OK"),
+    (dict(N=0, g=0, lse=0, hidden=0, targets=0, ws=0, dw=0xA0000008), "FLP_MISALIGNED"),
+    (dict(N=0, g=0, lse=0, hidden=0, targets=0, ws=0, db=0xB0000002), "FLP_MISALIGNED"),
+    (dict(N=0, g=0, lse=0, hidden=0, targets=0, ws=0, db=0xA0000000 + 64), "FLP_INVALID_ARGUMENT"),
+    (dict(N=0, g=0, lse=0, hidden=0, targets=0, ws=0, dw=W), "FLP_INVALID_ARGUMENT"),
 ])
 def test_backward_gates(kw, expect):
     assert abi.STATUS_NAMES[bwd(**kw)] == expect
@@ -292,7 +297,9 @@ def ibwd(**kw):
     (dict(g=0), "FLP_INVALID_ARGUMENT"),
     (dict(wsb=4096), "FLP_WORKSPACE_TOO_SMALL"),
     (dict(dh=0, dw=0, db=0, ws=0), "FLP_OK"),           # nothing requested: no-op
-    (dict(N=0, g=0, lse=0, hidden=0, targets=0, ws=0), "FLP_OK"),
+    (dict(N=0, g=0, lse=0, hidden=0, targets=0, ws=0, dw=0, db=0), "FLP_OK"),
+    (dict(N=0, g=0, lse=0, hidden=0, targets=0, ws=0, dw=0xA0000008), "FLP_MISALIGNED"),
+    (dict(N=0, g=0, lse=0, hidden=0, targets=0, ws=0, dw=0, db=B), "FLP_INVALID_ARGUMENT"),
 ])
 def test_backward_indexed_gates(kw, expect):
     assert abi.STATUS_NAMES[ibwd(**kw)] == expect
@@ -400,7 +407,9 @@ def ebwd(**kw):
     (dict(dw=0x90000004), "FLP_MISALIGNED"),
     (dict(dw=H), "FLP_INVALID_ARGUMENT"),               # d_weight overlaps grad
     (dict(ws=0x90000000 + 1024), "FLP_INVALID_ARGUMENT"),  # workspace inside d_weight
-    (dict(N=0, g=0, ids=0, dw=0, ws=0), "FLP_OK"),
+    # empty batch: d_weight is still written (zeros), so it is required and checked
+    (dict(N=0, g=0, ids=0, dw=0, ws=0), "FLP_INVALID_ARGUMENT"),
+    (dict(N=0, g=0, ids=0, dw=0x90000004, ws=0), "FLP_MISALIGNED"),
 ])
 def test_embedding_backward_gates(kw, expect):
     assert abi.STATUS_NAMES[ebwd(**kw)] == expect

@@ -62,6 +62,43 @@ def test_empty_batch_is_a_noop():
     assert lp.shape == (0,) and ls.shape == (0,)
 
 
+def test_empty_batch_zeroes_the_sums():
+    """N = 0: the backward calls write d_weight and d_bias as zeros (sums over no rows)."""
+    m = flp()
+    d = "cuda:0"
+    D, V = 128, 500
+    s = torch.cuda.current_stream().cuda_stream
+    w = torch.randn(V, D, device=d).to(torch.bfloat16)
+    for dwt, code in ((torch.bfloat16, m.FLP_BF16), (torch.float32, m.FLP_F32)):
+        dw = torch.full((V, D), 7.0, device=d, dtype=dwt)
+        db = torch.full((V,), 7.0, device=d)
+        st = m.flp_backward(0, D, V, m.FLP_BF16, 0, 0, 0, w.data_ptr(), 0, 0, m.FLP_I64, 0, 0,
+                            dw.data_ptr(), code, db.data_ptr(), 0, 0, s)
+        torch.cuda.synchronize()
+        assert st == m.FLP_OK and not dw.any() and not db.any()
+        dw.fill_(7.0)
+        db.fill_(7.0)
+        st = m.flp_backward_indexed(0, D, V, m.FLP_BF16, 0, 0, 0, w.data_ptr(), 0, 0, m.FLP_I64,
+                                    0, 0, m.FLP_I64, 0, 0, dw.data_ptr(), code, db.data_ptr(), 0,
+                                    0, s)
+        torch.cuda.synchronize()
+        assert st == m.FLP_OK and not dw.any() and not db.any()
+        dw.fill_(7.0)
+        st = m.flp_embedding_backward(0, D, V, m.FLP_BF16, 0, 0, m.FLP_I64, dw.data_ptr(), code,
+                                      0, 0, s)
+        torch.cuda.synchronize()
+        assert st == m.FLP_OK and not dw.any()
+    # the same through the torch layer
+    h = torch.empty(0, D, dtype=torch.bfloat16, device=d)
+    t = torch.empty(0, dtype=torch.int64, device=d)
+    z = torch.empty(0, device=d)
+    b = torch.randn(V, device=d)
+    dh, dw, db = m.backward(z, z, h, w, t, b)
+    torch.cuda.synchronize()
+    assert dh.shape == (0, D) and not dw.any() and not db.any()
+    assert not m.embedding_backward(h, t, V).any()
+
+
 def test_python_layer_rejects_bad_tensors():
     m = flp()
     b = _bufs()
