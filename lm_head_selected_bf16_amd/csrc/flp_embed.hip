@@ -16,6 +16,11 @@
 // wave: inside a group every run of equal ids is summed in fp32 in token order;
 // a segment that spans several groups adds its per-group pieces in group order.
 // Every order is fixed by the sorted list: the output is bitwise reproducible.
+//
+// The rows of ids that do not occur are most of d_E's bytes.  The sort's
+// scatter passes occupy few compute units, so their launches (and the group
+// pass) carry extra "rider" workgroups that write those zero rows alongside;
+// the first sort pass marks the ids that occur before any rider runs.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -52,6 +57,27 @@ __global__ __launch_bounds__(256) void k_embed_fwd(const u32x4* __restrict__ wei
   }
 }
 
+// Zero rows of ids that do not occur, written by workgroups appended to another
+// kernel's grid: workgroup r of the riders clears rows v0 + 4 r .. v0 + 4 r + 3 of
+// [v0, v1) (one wave per row) whose id is unmarked.  seg_end[v] != 0 marks an id
+// that occurs (set by the first sort pass, later overwritten by its segment end,
+// which is never 0).
+struct ZeroRider {
+  u32x4* dW;               // d_E [V][row_vec]
+  const int32_t* seg_end;  // [V]
+  int64_t v0, v1;          // rows of this launch
+  int64_t row_vec;         // 16-byte chunks per d_E row
+  int64_t blocks() const { return (v1 - v0 + 3) / 4; }
+};
+
+__device__ __forceinline__ void ride(const ZeroRider& z, int64_t r) {
+  const int64_t v = z.v0 + r * 4 + (threadIdx.x >> 6);
+  if (v >= z.v1 || z.seg_end[v] != 0) return;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  u32x4* row = z.dW + v * z.row_vec;
+  for (int64_t c = threadIdx.x & 63; c < z.row_vec; c += 64) __builtin_nontemporal_store(zero, row + c);
+}
+
 // Sort keys: the id, or V for an id outside [0, V) (those sort last and are
 // dropped); values: the token index.  The same grid clears the [V] segment
 // bounds (an id that does not occur keeps an empty segment).
@@ -71,10 +97,12 @@ __global__ __launch_bounds__(256) void k_sort_init(const void* __restrict__ ids,
   vals[i] = int32_t(i);
 }
 
-// Per-block digit counts, stored digit-major: hist[d * n_blocks + b].
+// Per-block digit counts, stored digit-major: hist[d * n_blocks + b].  With
+// `mark` set (the first pass), also marks every id that occurs: mark[id] = 1.
 __global__ __launch_bounds__(256) void k_sort_hist(const uint32_t* __restrict__ keys, int64_t n,
                                                    int shift, int64_t n_blocks,
-                                                   int32_t* __restrict__ hist) {
+                                                   int32_t* __restrict__ hist,
+                                                   int32_t* __restrict__ mark, int64_t V) {
   __shared__ int32_t cnt[256];
   const int t = threadIdx.x;
   const int64_t b = blockIdx.x;
@@ -82,7 +110,11 @@ __global__ __launch_bounds__(256) void k_sort_hist(const uint32_t* __restrict__ 
   __syncthreads();
   for (int k = t; k < kSortBlock; k += 256) {
     const int64_t i = b * kSortBlock + k;
-    if (i < n) atomicAdd(&cnt[(keys[i] >> shift) & 255u], 1);
+    if (i < n) {
+      const uint32_t key = keys[i];
+      atomicAdd(&cnt[(key >> shift) & 255u], 1);
+      if (mark != nullptr && int64_t(key) < V) mark[key] = 1;
+    }
   }
   __syncthreads();
   hist[int64_t(t) * n_blocks + b] = cnt[t];
@@ -98,7 +130,11 @@ __global__ __launch_bounds__(256) void k_sort_scatter(const uint32_t* __restrict
                                                       int shift, int64_t n_blocks,
                                                       const int32_t* __restrict__ hist,
                                                       uint32_t* __restrict__ kout,
-                                                      int32_t* __restrict__ vout) {
+                                                      int32_t* __restrict__ vout, ZeroRider z) {
+  if (int64_t(blockIdx.x) >= n_blocks) {
+    ride(z, int64_t(blockIdx.x) - n_blocks);
+    return;
+  }
   __shared__ int32_t tot[256];
   __shared__ int32_t run[256];
   __shared__ int32_t dig[256];
@@ -259,7 +295,12 @@ __global__ __launch_bounds__(256) void k_embed_runs(const u32x4* __restrict__ gr
                                                     const int32_t* __restrict__ seg_end, int64_t N,
                                                     int64_t V, int64_t row_vec,
                                                     float* __restrict__ head,
-                                                    float* __restrict__ tail, void* __restrict__ dW) {
+                                                    float* __restrict__ tail, void* __restrict__ dW,
+                                                    int64_t n_groups, ZeroRider z) {
+  if (int64_t(blockIdx.x) >= n_groups) {
+    ride(z, int64_t(blockIdx.x) - n_groups);
+    return;
+  }
   constexpr int EPC = 16 / XS;
   __shared__ uint32_t skey[kSegGroup];
   __shared__ int32_t stok[kSegGroup];
@@ -317,10 +358,13 @@ __global__ __launch_bounds__(256) void k_embed_runs(const u32x4* __restrict__ gr
   }
 }
 
-// Pass B: one wave per vocabulary row, four rows per workgroup.  An id that does
-// not occur gets a zero row; an id whose segment spans several groups adds its
-// pieces in group order (the first group's head or tail slot, then the head
-// slots of the following groups); an id inside one group was written by pass A.
+// Pass B: an id whose segment spans several groups adds its pieces in group
+// order (the first group's head or tail slot, then the head slots of the
+// following groups); an id inside one group was written by pass A, and an id
+// that does not occur by a zero-row rider.  Workgroup b of B tests the ids b,
+// b + B, ..., one per thread (the stride spreads frequent ids, which are often
+// neighbours, over many workgroups), lists the spanning ones in LDS, then
+// combines them one after another with all 256 threads, eight pieces in flight.
 template <int XS, bool OUT_F32>
 __global__ __launch_bounds__(256) void k_embed_rows(const int32_t* __restrict__ seg_begin,
                                                     const int32_t* __restrict__ seg_end,
@@ -329,32 +373,39 @@ __global__ __launch_bounds__(256) void k_embed_rows(const int32_t* __restrict__ 
                                                     const float* __restrict__ tail, int f16,
                                                     void* __restrict__ dW) {
   constexpr int EPC = 16 / XS;
-  const int lane = threadIdx.x & 63;
-  const int64_t v = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (v >= V) return;
-  const int64_t b = seg_begin[v], e = seg_end[v];
-  const int64_t g0 = b / kSegGroup, g1 = (e - 1) / kSegGroup;
-  if (e > b && g0 == g1) return;
-  const float* first = (b == g0 * kSegGroup) ? head : tail;
-  for (int64_t c = lane; c < row_vec; c += 64) {
-    float acc[EPC];
-#pragma unroll
-    for (int q = 0; q < EPC; ++q) acc[q] = 0.0f;
-    if (e > b) {
+  __shared__ int32_t list[256];
+  __shared__ int32_t count;
+  const int t = threadIdx.x;
+  const int64_t v_t = int64_t(blockIdx.x) + int64_t(t) * gridDim.x;
+  if (t == 0) count = 0;
+  __syncthreads();
+  if (v_t < V) {
+    const int32_t b = seg_begin[v_t], e = seg_end[v_t];
+    if (e > b && b / kSegGroup != (e - 1) / kSegGroup) list[atomicAdd(&count, 1)] = t;
+  }
+  __syncthreads();
+  const int n = count;
+  for (int k = 0; k < n; ++k) {
+    const int64_t v = int64_t(blockIdx.x) + int64_t(list[k]) * gridDim.x;
+    const int64_t b = seg_begin[v], e = seg_end[v];
+    const int64_t g0 = b / kSegGroup, g1 = (e - 1) / kSegGroup;
+    const float* first = (b == g0 * kSegGroup) ? head : tail;
+    for (int64_t c = t; c < row_vec; c += 256) {
+      float acc[EPC];
       const float* f = first + (g0 * row_vec + c) * EPC;
 #pragma unroll
       for (int q = 0; q < EPC; ++q) acc[q] = f[q];
       int64_t g = g0 + 1;
-      for (; g + 4 <= g1 + 1; g += 4) {  // four pieces in flight, added in group order
-        float x[4][EPC];
+      for (; g + 8 <= g1 + 1; g += 8) {  // eight pieces in flight, added in group order
+        float x[8][EPC];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 8; ++u) {
           const float* h = head + ((g + u) * row_vec + c) * EPC;
 #pragma unroll
           for (int q = 0; q < EPC; ++q) x[u][q] = h[q];
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < 8; ++u)
 #pragma unroll
           for (int q = 0; q < EPC; ++q) acc[q] += x[u][q];
       }
@@ -363,8 +414,8 @@ __global__ __launch_bounds__(256) void k_embed_rows(const int32_t* __restrict__ 
 #pragma unroll
         for (int q = 0; q < EPC; ++q) acc[q] += h[q];
       }
+      store_chunk<XS, OUT_F32>(acc, dW, v, row_vec, c, f16 != 0);
     }
-    store_chunk<XS, OUT_F32>(acc, dW, v, row_vec, c, f16 != 0);
   }
 }
 
@@ -394,35 +445,60 @@ hipError_t launch_embedding_backward(const EmbedBwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_sort_init, dim3(unsigned((init_n + 255) / 256)), dim3(256), 0, s, a.ids,
                      int(a.i64), N, V, a.keys[0], a.vals[0], a.seg_begin, a.seg_end);
   const int passes = embed_sort_passes(V);
+  // Zero rows ride on the scatter launches (latency-bound, with most compute
+  // units idle) and on the group pass: the group pass takes the upper half of
+  // the rows, the scatters share the lower half evenly.
+  ZeroRider z{};
+  z.dW = static_cast<u32x4*>(a.d_weight);
+  z.seg_end = a.seg_end;
+  z.row_vec = a.D * int64_t(dtype_size(a.dw)) / 16;
+  const int64_t lower = V - V / 2;
+  const int n_sort_slices = passes;
+  int slice = 0;
+  auto next_slice = [&]() {
+    ZeroRider r = z;
+    r.v0 = lower * slice / n_sort_slices;
+    r.v1 = lower * (slice + 1) / n_sort_slices;
+    ++slice;
+    return r;
+  };
   for (int p = 0; p < passes; ++p) {
     const int src = p & 1, dst = src ^ 1;
     hipLaunchKernelGGL(k_sort_hist, dim3(unsigned(n_blocks)), dim3(256), 0, s, a.keys[src], N,
-                       8 * p, n_blocks, a.hist);
-    hipLaunchKernelGGL(k_sort_scatter, dim3(unsigned(n_blocks)), dim3(256), 0, s, a.keys[src],
-                       a.vals[src], N, 8 * p, n_blocks, a.hist, a.keys[dst], a.vals[dst]);
+                       8 * p, n_blocks, a.hist, p == 0 ? a.seg_end : nullptr, V);
+    const ZeroRider zs = next_slice();
+    hipLaunchKernelGGL(k_sort_scatter, dim3(unsigned(n_blocks + zs.blocks())), dim3(256), 0, s,
+                       a.keys[src], a.vals[src], N, 8 * p, n_blocks, a.hist, a.keys[dst],
+                       a.vals[dst], zs);
   }
   const int fin = passes & 1;
   hipLaunchKernelGGL(k_seg_bounds, dim3(unsigned((N + 255) / 256)), dim3(256), 0, s, a.keys[fin],
                      N, V, a.seg_begin, a.seg_end);
   const int64_t row_vec = a.D * int64_t(dtype_size(a.x)) / 16;
-  const dim3 ga(unsigned((N + kSegGroup - 1) / kSegGroup)), gb(unsigned((V + 3) / 4));
+  const int64_t n_groups = (N + kSegGroup - 1) / kSegGroup;
+  ZeroRider zr = z;
+  zr.v0 = lower;
+  zr.v1 = V;
+  const dim3 ga(unsigned(n_groups + zr.blocks())), gb(unsigned((V + 255) / 256));
   const int f16 = a.x == FLP_F16 ? 1 : 0;
   const u32x4* g = static_cast<const u32x4*>(a.grad);
   const uint32_t* keys = a.keys[fin];
   const int32_t* tok = a.vals[fin];
   if (a.x == FLP_F32) {
     hipLaunchKernelGGL((k_embed_runs<4, true>), ga, dim3(256), 0, s, g, 0, keys, tok, a.seg_begin,
-                       a.seg_end, N, V, row_vec, a.head, a.tail, a.d_weight);
+                       a.seg_end, N, V, row_vec, a.head, a.tail, a.d_weight, n_groups, zr);
     hipLaunchKernelGGL((k_embed_rows<4, true>), gb, dim3(256), 0, s, a.seg_begin, a.seg_end, V,
                        row_vec, a.head, a.tail, 0, a.d_weight);
   } else if (a.dw == FLP_F32) {
     hipLaunchKernelGGL((k_embed_runs<2, true>), ga, dim3(256), 0, s, g, f16, keys, tok,
-                       a.seg_begin, a.seg_end, N, V, row_vec, a.head, a.tail, a.d_weight);
+                       a.seg_begin, a.seg_end, N, V, row_vec, a.head, a.tail, a.d_weight,
+                       n_groups, zr);
     hipLaunchKernelGGL((k_embed_rows<2, true>), gb, dim3(256), 0, s, a.seg_begin, a.seg_end, V,
                        row_vec, a.head, a.tail, f16, a.d_weight);
   } else {
     hipLaunchKernelGGL((k_embed_runs<2, false>), ga, dim3(256), 0, s, g, f16, keys, tok,
-                       a.seg_begin, a.seg_end, N, V, row_vec, a.head, a.tail, a.d_weight);
+                       a.seg_begin, a.seg_end, N, V, row_vec, a.head, a.tail, a.d_weight,
+                       n_groups, zr);
     hipLaunchKernelGGL((k_embed_rows<2, false>), gb, dim3(256), 0, s, a.seg_begin, a.seg_end, V,
                        row_vec, a.head, a.tail, f16, a.d_weight);
   }

@@ -1189,8 +1189,8 @@ const char* kernel_ids() {
          "k_gemm dX, dW<256x224, 4x2 waves, K-blocked operands>; k_transpose (K-blocked); "
          "k_dbias_fold; k_fill; k_logits_fwd, k_logits_bwd<one wave per row>; "
          "rows: k_mark, k_compact, k_gather, k_scatter_rows, k_scatter_hidden; "
-         "embedding: k_embed_fwd, radix sort (k_sort_hist, k_scan_excl, k_sort_scatter), "
-         "k_seg_bounds, k_embed_bwd";
+         "embedding: k_embed_fwd, radix sort (k_sort_init, k_sort_hist, k_sort_scatter; zero-row "
+         "riders), k_seg_bounds, k_embed_runs<32-position groups>, k_embed_rows";
 }
 
 }  // namespace flp
