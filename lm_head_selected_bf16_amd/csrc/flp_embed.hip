@@ -310,7 +310,7 @@ __global__ __launch_bounds__(256) void k_embed_runs(const u32x4* __restrict__ gr
   const int n = int((N - s0) < kSegGroup ? (N - s0) : kSegGroup);
   if (threadIdx.x < kSegGroup) {
     // positions past the batch and dropped ids read as key V (never summed)
-    const bool in = threadIdx.x < n;
+    const bool in = int(threadIdx.x) < n;
     const uint32_t k = in ? keys[s0 + threadIdx.x] : uint32_t(V);
     const bool live = in && int64_t(k) < V;
     skey[threadIdx.x] = k;

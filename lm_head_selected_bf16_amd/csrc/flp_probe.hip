@@ -115,10 +115,10 @@ hipError_t probe_mfma(int zero, int64_t iters, void* scratch, hipStream_t s, dou
   if (e == hipSuccess) {
     // one untimed launch brings the clock to its sustained state
     hipLaunchKernelGGL(k_probe_mfma, dim3(kProbeWG), dim3(256), 0, s, iters, zero, out, clk);
-    hipEventRecord(a, s);
+    e = hipEventRecord(a, s);
     hipLaunchKernelGGL(k_probe_mfma, dim3(kProbeWG), dim3(256), 0, s, iters, zero, out, clk);
-    hipEventRecord(b, s);
-    e = hipGetLastError();
+    if (e == hipSuccess) e = hipEventRecord(b, s);
+    if (e == hipSuccess) e = hipGetLastError();
   }
   std::vector<uint64_t> host(2 * size_t(kProbeWG));
   if (e == hipSuccess) e = hipEventSynchronize(b);
@@ -130,8 +130,8 @@ hipError_t probe_mfma(int zero, int64_t iters, void* scratch, hipStream_t s, dou
   int dev = 0, wall_khz = 0;
   if (e == hipSuccess) e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&wall_khz, hipDeviceAttributeWallClockRate, dev);
-  if (a != nullptr) hipEventDestroy(a);
-  if (b != nullptr) hipEventDestroy(b);
+  if (a != nullptr) (void)hipEventDestroy(a);
+  if (b != nullptr) (void)hipEventDestroy(b);
   if (e != hipSuccess) return e;
   const double flops = double(kProbeWG) * 4.0 * double(iters) * 128.0 * (16.0 * 16.0 * 32.0 * 2.0);
   *tflops = flops / (double(ms) * 1e-3) / 1e12;
@@ -153,17 +153,17 @@ hipError_t probe_read(const void* buf, size_t bytes, void* scratch, hipStream_t 
   if (e == hipSuccess) {
     hipLaunchKernelGGL(k_probe_read, dim3(grid), dim3(256), 0, s, static_cast<const u32x4*>(buf), n,
                        static_cast<uint32_t*>(scratch));
-    hipEventRecord(a, s);
+    e = hipEventRecord(a, s);
     for (int r = 0; r < 5; ++r)
       hipLaunchKernelGGL(k_probe_read, dim3(grid), dim3(256), 0, s, static_cast<const u32x4*>(buf),
                          n, static_cast<uint32_t*>(scratch));
-    hipEventRecord(b, s);
-    e = hipGetLastError();
+    if (e == hipSuccess) e = hipEventRecord(b, s);
+    if (e == hipSuccess) e = hipGetLastError();
   }
   if (e == hipSuccess) e = hipEventSynchronize(b);
   if (e == hipSuccess) e = hipEventElapsedTime(&ms, a, b);
-  if (a != nullptr) hipEventDestroy(a);
-  if (b != nullptr) hipEventDestroy(b);
+  if (a != nullptr) (void)hipEventDestroy(a);
+  if (b != nullptr) (void)hipEventDestroy(b);
   if (e != hipSuccess) return e;
   *gbs = double(n) * 16.0 * 5.0 / (double(ms) * 1e-3) / 1e9;
   return hipSuccess;
