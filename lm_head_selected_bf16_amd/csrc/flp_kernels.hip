@@ -37,6 +37,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include <math.h>
 
 #include "flp_launch.h"
@@ -983,18 +985,29 @@ __global__ __launch_bounds__(256) void k_dbias_fold(const float* part, int64_t n
 
 // ---- launch helpers ----------------------------------------------------------------------------
 
+// Dynamic LDS above 64 KiB must be opted into per kernel and device.  Each launch
+// site keeps a per-device record of having done so; two threads that race on the
+// first launch both set the same attribute.
+constexpr int kMaxDevices = 64;
 template <class K>
-hipError_t prepare(K kernel, size_t lds) {
-  // Dynamic LDS above 64 KiB must be opted into once per kernel.
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+hipError_t prepare(K kernel, size_t lds, std::atomic<int> (&ready)[kMaxDevices]) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const bool tracked = dev >= 0 && dev < kMaxDevices;
+  if (tracked && ready[dev].load(std::memory_order_acquire) != 0) return hipSuccess;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  if (e == hipSuccess && tracked) ready[dev].store(1, std::memory_order_release);
+  return e;
 }
 
 template <class E, int BM, int WM, bool ODD>
 hipError_t fwd_cfg(const FwdArgs& a, hipStream_t s) {
   using Eng = LogitEngine<E, BM, WM>;
-  static hipError_t once = prepare(k_fwd<E, BM, WM, ODD>, Eng::kLds);
-  if (once != hipSuccess) return once;
+  static std::atomic<int> ready[kMaxDevices];
+  const hipError_t e = prepare(k_fwd<E, BM, WM, ODD>, Eng::kLds, ready);
+  if (e != hipSuccess) return e;
   const int64_t blocks = ((a.N + BM - 1) / BM) * ((a.V + kTileCols - 1) / kTileCols);
   hipLaunchKernelGGL((k_fwd<E, BM, WM, ODD>), dim3(unsigned(blocks)), dim3(Eng::NT), Eng::kLds, s,
                      a);
@@ -1024,8 +1037,9 @@ template <class E, int BM, int WM, bool ODD>
 hipError_t dz_cfg(const DzArgs& a, hipStream_t s) {
   using Eng = LogitEngine<E, BM, WM>;
   constexpr size_t lds = dz_lds<E, BM, WM>();
-  static hipError_t once = prepare(k_dz<E, BM, WM, ODD>, lds);
-  if (once != hipSuccess) return once;
+  static std::atomic<int> ready[kMaxDevices];
+  const hipError_t e = prepare(k_dz<E, BM, WM, ODD>, lds, ready);
+  if (e != hipSuccess) return e;
   const int64_t blocks = ((a.rows + BM - 1) / BM) * ((a.V + kTileCols - 1) / kTileCols);
   hipLaunchKernelGGL((k_dz<E, BM, WM, ODD>), dim3(unsigned(blocks)), dim3(Eng::NT), lds, s, a);
   return hipGetLastError();
@@ -1034,8 +1048,9 @@ hipError_t dz_cfg(const DzArgs& a, hipStream_t s) {
 template <class E, int BM, int BN, int WM, int WN, bool LOAD, int STORE>
 hipError_t gemm_cfg(const GemmArgs& a, hipStream_t s) {
   using Eng = Engine<E, BM, BN, WM, WN>;
-  static hipError_t once = prepare(k_gemm<E, BM, BN, WM, WN, LOAD, STORE>, Eng::kLds);
-  if (once != hipSuccess) return once;
+  static std::atomic<int> ready[kMaxDevices];
+  const hipError_t e = prepare(k_gemm<E, BM, BN, WM, WN, LOAD, STORE>, Eng::kLds, ready);
+  if (e != hipSuccess) return e;
   const int64_t blocks = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   hipLaunchKernelGGL((k_gemm<E, BM, BN, WM, WN, LOAD, STORE>), dim3(unsigned(blocks)),
                      dim3(Eng::NT), Eng::kLds, s, a);
