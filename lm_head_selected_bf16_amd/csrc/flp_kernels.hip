@@ -70,6 +70,17 @@ struct F32 {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// x of lane l ^ m.  For m = 1 and 2 a DPP quad permutation ([1, 0, 3, 2] and
+// [2, 3, 0, 1]) and for m = 8 a rotation by 8 within the 16-lane row do it as a
+// VALU move; other distances go through ds_bpermute.
+__device__ __forceinline__ float lane_xor(float x, int m) {
+  const int b = __float_as_int(x);
+  if (m == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0xB1, 0xF, 0xF, true));
+  if (m == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0x4E, 0xF, 0xF, true));
+  if (m == 8) return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0x128, 0xF, 0xF, true));
+  return __shfl_xor(x, m);
+}
+
 // 64 bytes of K per lane quad: one bf16 16x16x32 MFMA, or four fp32 16x16x4
 // MFMAs over the same 16 bytes per lane (K index 4g + t in instruction t).
 template <class E>
@@ -825,8 +836,8 @@ __global__ __launch_bounds__(128 * WM) void k_dz(DzArgs p) {
           const f32x4_t d = acc[mb][nb];
           const float x0 = even ? d[2] : d[0];
           const float x1 = even ? d[3] : d[1];
-          const float y0 = __shfl_xor(x0, 1);
-          const float y1 = __shfl_xor(x1, 1);
+          const float y0 = lane_xor(x0, 1);
+          const float y1 = lane_xor(x1, 1);
           const int te = wm * RW + mb * 16 + (i & ~1);  // even token of the pair
           const int c = wn * kHalfCols + nb * 16 + 4 * g + (even ? 0 : 2);
           const float lo0 = even ? d[0] : y0, hi0 = even ? y0 : d[2];
@@ -844,21 +855,37 @@ __global__ __launch_bounds__(128 * WM) void k_dz(DzArgs p) {
     }
   }
   if (p.dbias_part == nullptr) return;
-  // Column sums over the tile's rows: in-lane over row blocks, then a butterfly
-  // over the 16 lanes holding the other rows, then ascending over row waves.
+  // Column sums over the tile's rows: in-lane over row blocks, then over the 16
+  // lanes holding the other rows, then ascending over row waves.  The 16-lane step
+  // is a reduce-scatter: a lane holds 32 column values (j = 4 nb + r); at the step
+  // over lane bit m it keeps the half of its values that bit selects and adds the
+  // partner's copy of that half, so after the four steps lane i holds the finished
+  // sums of columns j = 2i and 2i + 1 (30 exchanges instead of 128).
+  static_assert(WNB == 8, "the column reduction is laid out for 32 values per lane");
   __syncthreads();
   float* red = reinterpret_cast<float*>(smem);  // [WM][256]
+  {
+    float v[4 * WNB];
 #pragma unroll
-  for (int nb = 0; nb < WNB; ++nb)
+    for (int nb = 0; nb < WNB; ++nb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float x = csum[nb][r];
-      x += __shfl_xor(x, 1);
-      x += __shfl_xor(x, 2);
-      x += __shfl_xor(x, 4);
-      x += __shfl_xor(x, 8);
-      if (i == 0) red[wm * kTileCols + wn * kHalfCols + nb * 16 + 4 * g + r] = x;
+      for (int r = 0; r < 4; ++r) v[4 * nb + r] = csum[nb][r];
+#pragma unroll
+    for (int h = 2 * WNB, m = 8; h >= 2; h >>= 1, m >>= 1) {
+      const bool up = (i & m) != 0;
+#pragma unroll
+      for (int k = 0; k < h; ++k) {
+        const float send = up ? v[k] : v[k + h];
+        const float keep = up ? v[k + h] : v[k];
+        v[k] = keep + lane_xor(send, m);
+      }
     }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int j = 2 * i + e;
+      red[wm * kTileCols + wn * kHalfCols + (j >> 2) * 16 + 4 * g + (j & 3)] = v[e];
+    }
+  }
   __syncthreads();
   for (int c = tid; c < kTileCols; c += NT) {
     float s = red[c];
