@@ -106,18 +106,17 @@ __device__ __forceinline__ void mma64<F32>(f32x4_t& c, const u32x4& a, const u32
   c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
-// Bits of a 16-bit element type, rounded to nearest even.
+// Bits of a 16-bit element type, rounded to nearest even.  gfx950 converts fp32
+// to bf16 in hardware (v_cvt_pk_bf16_f32, round to nearest even, denormals kept:
+// bit for bit the rounding (u + 0x7FFF + ((u >> 16) & 1)) >> 16 of the fp32 bits
+// for every finite value).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 template <class E>
 __device__ __forceinline__ uint32_t bits16(float f);
 template <>
 __device__ __forceinline__ uint32_t bits16<BF16>(float f) {
-  return bf16_bits_rne(f);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 template <>
 __device__ __forceinline__ uint32_t bits16<F16>(float f) {
@@ -126,6 +125,11 @@ __device__ __forceinline__ uint32_t bits16<F16>(float f) {
 template <class E>
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   return bits16<E>(lo) | (bits16<E>(hi) << 16);
+}
+template <>
+__device__ __forceinline__ uint32_t pack2<BF16>(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // Store four consecutive fp32 values as the element type.
@@ -411,15 +415,29 @@ __global__ __launch_bounds__(128 * WM) void k_fwd(FwdArgs p) {
 
   float* red = reinterpret_cast<float*>(smem);  // [2][BM] row max, then [2][BM] row sums
   const int64_t cw = col0 + wn * kHalfCols;
+  // Columns of this wave at or past lim are vocabulary padding (lim < 128 only in
+  // the last vocabulary tile).
+  const int lim = int(p.V - cw < kHalfCols ? p.V - cw : kHalfCols);
   float bcol[WNB][4];
 #pragma unroll
   for (int nb = 0; nb < WNB; ++nb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t c = cw + nb * 16 + 4 * g + r;
-      bcol[nb][r] = (p.bias != nullptr && c < p.V) ? p.bias[c] : 0.f;
+    for (int r = 0; r < 4; ++r) bcol[nb][r] = 0.f;
+  if (p.bias != nullptr) {
+    const float* bw = p.bias + cw + 4 * g;
+    if (lim == kHalfCols) {  // wave-uniform: every column of the wave exists
+#pragma unroll
+      for (int nb = 0; nb < WNB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) bcol[nb][r] = bw[nb * 16 + r];
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < WNB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (nb * 16 + 4 * g + r < lim) bcol[nb][r] = bw[nb * 16 + r];
     }
-  const int64_t vlim = p.V - cw;  // columns of this wave at or past vlim are padding
+  }
 
 #pragma unroll
   for (int mb = 0; mb < WMB; ++mb) {
@@ -432,7 +450,7 @@ __global__ __launch_bounds__(128 * WM) void k_fwd(FwdArgs p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float z = (acc[mb][nb][r] + bcol[nb][r]) * invT;
-        z = (nb * 16 + 4 * g + r < vlim) ? z : -INFINITY;
+        z = (nb * 16 + 4 * g + r < lim) ? z : -INFINITY;
         acc[mb][nb][r] = z;
         mx = fmaxf(mx, z);
       }
@@ -736,7 +754,9 @@ __global__ __launch_bounds__(128 * WM) void k_dz(DzArgs p) {
   __syncthreads();  // every wave is done with the operand stages: LDS is reused below
 
   const int64_t cw = col0 + wn * kHalfCols;
-  const int64_t vlim = p.V - cw;
+  // Columns of this wave at or past lim are vocabulary padding (lim < 128 only in
+  // the last vocabulary tile).
+  const int lim = int(p.V - cw < kHalfCols ? p.V - cw : kHalfCols);
   char* lds = reinterpret_cast<char*>(smem);
   f32x4_t csum[WNB];
   {
@@ -745,9 +765,21 @@ __global__ __launch_bounds__(128 * WM) void k_dz(DzArgs p) {
     for (int nb = 0; nb < WNB; ++nb) {
       csum[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t c = cw + nb * 16 + 4 * g + r;
-        bcol[nb][r] = (p.bias != nullptr && c < p.V) ? p.bias[c] : 0.f;
+      for (int r = 0; r < 4; ++r) bcol[nb][r] = 0.f;
+    }
+    if (p.bias != nullptr) {
+      const float* bw = p.bias + cw + 4 * g;
+      if (lim == kHalfCols) {  // wave-uniform: every column of the wave exists
+#pragma unroll
+        for (int nb = 0; nb < WNB; ++nb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) bcol[nb][r] = bw[nb * 16 + r];
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < WNB; ++nb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (nb * 16 + 4 * g + r < lim) bcol[nb][r] = bw[nb * 16 + r];
       }
     }
     // dz = G (onehot - exp(z - lse)) / T, kept in the accumulator registers.
@@ -760,7 +792,11 @@ __global__ __launch_bounds__(128 * WM) void k_dz(DzArgs p) {
       const bool valid = t >= 0 && t < p.V;
       const float G = valid ? p.grad_out[row] * invT : 0.f;
       const float L = rv ? p.lse[row] : 0.f;
+      // The target's column within the wave, or -1 when it lies elsewhere; the
+      // columns a valid row keeps are those below lim (none for an invalid row).
       const int64_t trel = t - cw;
+      const int tcol = (trel >= 0 && trel < kHalfCols) ? int(trel) : -1;
+      const int keep = valid ? lim : 0;
 #pragma unroll
       for (int nb = 0; nb < WNB; ++nb) {
         f32x4_t d;
@@ -769,9 +805,9 @@ __global__ __launch_bounds__(128 * WM) void k_dz(DzArgs p) {
           const int cl = nb * 16 + 4 * g + r;
           const float z = (acc[mb][nb][r] + bcol[nb][r]) * invT;
           const float pr = fast_exp2((z - L) * kLog2e);
-          const float oh = (cl == trel) ? 1.0f : 0.0f;
+          const float oh = (cl == tcol) ? 1.0f : 0.0f;
           float v = G * (oh - pr);
-          v = (valid && cl < vlim) ? v : 0.0f;
+          v = (cl < keep) ? v : 0.0f;
           d[r] = v;
         }
         csum[nb] += d;
