@@ -392,7 +392,8 @@ __global__ __launch_bounds__(128 * WM) void k_fwd(FwdArgs p) {
   using Eng = LogitEngine<E, BM, WM>;
   constexpr int RW = Eng::RW, WMB = Eng::WMB, WNB = Eng::WNB, NT = Eng::NT;
   extern __shared__ u32x4 smem[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: tile tests become scalar
   const int wm = wave % WM, wn = wave / WM, i = lane & 15, g = lane >> 4;
   const int nbm = int((p.N + BM - 1) / BM);
   const int nbn = int((p.V + kTileCols - 1) / kTileCols);
@@ -444,16 +445,22 @@ __global__ __launch_bounds__(128 * WM) void k_fwd(FwdArgs p) {
     const int rl = wm * RW + mb * 16 + i;
     const int64_t row = row0 + rl;
     const float invT = (p.temperature != nullptr && row < p.N) ? 1.0f / p.temperature[row] : 1.0f;
+#pragma unroll
+    for (int nb = 0; nb < WNB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[mb][nb][r] = (acc[mb][nb][r] + bcol[nb][r]) * invT;
+    if (lim < kHalfCols) {  // the last vocabulary tile: padding columns drop out
+#pragma unroll
+      for (int nb = 0; nb < WNB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (nb * 16 + 4 * g + r >= lim) acc[mb][nb][r] = -INFINITY;
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int nb = 0; nb < WNB; ++nb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float z = (acc[mb][nb][r] + bcol[nb][r]) * invT;
-        z = (nb * 16 + 4 * g + r < lim) ? z : -INFINITY;
-        acc[mb][nb][r] = z;
-        mx = fmaxf(mx, z);
-      }
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, acc[mb][nb][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     if (g == 0) red[wn * BM + rl] = mx;
@@ -464,11 +471,12 @@ __global__ __launch_bounds__(128 * WM) void k_fwd(FwdArgs p) {
     const int rl = wm * RW + mb * 16 + i;
     const int64_t row = row0 + rl;
     const float M = fmaxf(red[rl], red[BM + rl]);
+    const float Ml = M * kLog2e;
     float e[WNB][4];
 #pragma unroll
     for (int nb = 0; nb < WNB; ++nb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) e[nb][r] = fast_exp2((acc[mb][nb][r] - M) * kLog2e);
+      for (int r = 0; r < 4; ++r) e[nb][r] = fast_exp2(fmaf(acc[mb][nb][r], kLog2e, -Ml));
     float s = lane_sum<WNB>(e);
     s += __shfl_xor(s, 16);
     s += __shfl_xor(s, 32);
@@ -734,7 +742,8 @@ __global__ __launch_bounds__(128 * WM) void k_dz(DzArgs p) {
   constexpr int RW = Eng::RW, WMB = Eng::WMB, WNB = Eng::WNB, NT = Eng::NT;
   constexpr bool kStage = E::kSize == 2 && BM == kTileCols;  // 16-bit: coalesce through LDS
   extern __shared__ u32x4 smem[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: tile tests become scalar
   const int wm = wave % WM, wn = wave / WM, i = lane & 15, g = lane >> 4;
   const int nbm = int((p.rows + BM - 1) / BM);
   const int nbn = int((p.V + kTileCols - 1) / kTileCols);
