@@ -49,6 +49,8 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -69,6 +71,18 @@ struct F32 {
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Both halves of a 16-lane (32-lane) exchange: every lane gets the values of lanes
+// l and l ^ 16 (l ^ 32), lower row first (v_permlane16_swap / v_permlane32_swap, a
+// VALU move).  A commutative combine of the two equals the xor-butterfly step.
+__device__ __forceinline__ f32x2_t pair16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return f32x2_t{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ f32x2_t pair32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return f32x2_t{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
 
 // x of lane l ^ m.  For m = 1 and 2 a DPP quad permutation ([1, 0, 3, 2] and
 // [2, 3, 0, 1]) and for m = 8 a rotation by 8 within the 16-lane row do it as a
@@ -110,8 +124,6 @@ __device__ __forceinline__ void mma64<F32>(f32x4_t& c, const u32x4& a, const u32
 // to bf16 in hardware (v_cvt_pk_bf16_f32, round to nearest even, denormals kept:
 // bit for bit the rounding (u + 0x7FFF + ((u >> 16) & 1)) >> 16 of the fp32 bits
 // for every finite value).
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
 template <class E>
 __device__ __forceinline__ uint32_t bits16(float f);
 template <>
@@ -461,8 +473,10 @@ __global__ __launch_bounds__(128 * WM) void k_fwd(FwdArgs p) {
     for (int nb = 0; nb < WNB; ++nb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) mx = fmaxf(mx, acc[mb][nb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    f32x2_t q = pair16(mx);
+    mx = fmaxf(q.x, q.y);
+    q = pair32(mx);
+    mx = fmaxf(q.x, q.y);
     if (g == 0) red[wn * BM + rl] = mx;
   }
   __syncthreads();
@@ -478,8 +492,10 @@ __global__ __launch_bounds__(128 * WM) void k_fwd(FwdArgs p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) e[nb][r] = fast_exp2(fmaf(acc[mb][nb][r], kLog2e, -Ml));
     float s = lane_sum<WNB>(e);
-    s += __shfl_xor(s, 16);
-    s += __shfl_xor(s, 32);
+    f32x2_t q = pair16(s);
+    s = q.x + q.y;
+    q = pair32(s);
+    s = q.x + q.y;
     if (g == 0) red[2 * BM + wn * BM + rl] = s;
     if (row < p.N) {
       const int64_t t = load_target(p.targets, p.t64, row) - p.t_off;
