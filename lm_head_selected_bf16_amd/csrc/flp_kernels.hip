@@ -817,28 +817,60 @@ __global__ __launch_bounds__(128 * WM) void k_dz(DzArgs p) {
       const bool valid = t >= 0 && t < p.V;
       const float G = valid ? p.grad_out[row] * invT : 0.f;
       const float L = rv ? p.lse[row] : 0.f;
-      // The target's column within the wave, or -1 when it lies elsewhere; the
-      // columns a valid row keeps are those below lim (none for an invalid row).
+      // The target's column within the wave for a valid row, else -1.
       const int64_t trel = t - cw;
-      const int tcol = (trel >= 0 && trel < kHalfCols) ? int(trel) : -1;
-      const int keep = valid ? lim : 0;
+      const int tcol = (valid && trel >= 0 && trel < kHalfCols) ? int(trel) : -1;
+      // Every kept logit is G (0 - p) = (-G) p (bit for bit, except that a p that
+      // underflows to 0 gives a zero of the other sign); the target's entry,
+      // G (1 - p), is taken from the row's logit before the tile is overwritten.
+      // Few rows of a wave have their target among its 128 columns, so that part
+      // runs under a branch most waves skip.
+      float vt = 0.f;
+      if (tcol >= 0) {
+        float at = 0.f, bt = 0.f;
 #pragma unroll
-      for (int nb = 0; nb < WNB; ++nb) {
-        f32x4_t d;
+        for (int nb = 0; nb < WNB; ++nb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (nb * 16 + 4 * g + r == tcol) {
+              at = acc[mb][nb][r];
+              bt = bcol[nb][r];
+            }
+        const float z = (at + bt) * invT;
+        vt = G * (1.0f - fast_exp2((z - L) * kLog2e));
+      }
+      const float nG = -G;
+#pragma unroll
+      for (int nb = 0; nb < WNB; ++nb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int cl = nb * 16 + 4 * g + r;
           const float z = (acc[mb][nb][r] + bcol[nb][r]) * invT;
-          const float pr = fast_exp2((z - L) * kLog2e);
-          const float oh = (cl == tcol) ? 1.0f : 0.0f;
-          float v = G * (oh - pr);
-          v = (cl < keep) ? v : 0.0f;
-          d[r] = v;
+          acc[mb][nb][r] = nG * fast_exp2((z - L) * kLog2e);
         }
+      if (tcol >= 0) {
+#pragma unroll
+        for (int nb = 0; nb < WNB; ++nb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (nb * 16 + 4 * g + r == tcol) acc[mb][nb][r] = vt;
+      }
+      // Rows with an ignored target and the vocabulary padding get zeros (+0).
+      if (!valid) {
+#pragma unroll
+        for (int nb = 0; nb < WNB; ++nb) acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+      if (lim < kHalfCols) {  // wave-uniform: the last vocabulary tile only
+#pragma unroll
+        for (int nb = 0; nb < WNB; ++nb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (nb * 16 + 4 * g + r >= lim) acc[mb][nb][r] = 0.f;
+      }
+#pragma unroll
+      for (int nb = 0; nb < WNB; ++nb) {
+        const f32x4_t d = acc[mb][nb];
         csum[nb] += d;
-        if constexpr (kStage) {
-          acc[mb][nb] = d;
-        } else {
+        if constexpr (!kStage) {
           constexpr int KB = 128 / E::kSize;
           const int64_t c = cw + nb * 16 + 4 * g;
           if (p.dz != nullptr) store4<E>(p.dz, kblk<KB>(row, c, p.ldt), d);
