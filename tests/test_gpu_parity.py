@@ -90,6 +90,25 @@ def test_small_ragged(k):
     full_check(inp, to_gpu(inp), case[0])
 
 
+@pytest.mark.parametrize("dtype", [BF16, torch.float32])
+def test_targets_at_tile_edges(dtype):
+    """Targets placed where the logit-tile epilogues branch: every row's target in
+    the last, ragged vocabulary tile (on the last real column, the first column of
+    a tile or of a wave's half, or a column near them), rows whose target sits in
+    the other half of a tile, and ignored rows mixed in, with bias and
+    temperature."""
+    N, D, V = 260, 256, 1000  # V = 3 * 256 + 232: the last tile has 232 real columns
+    w = flp_inputs.Workload("edges", 77, N, D, V, dtype, w_std=1.0 / np.sqrt(D) * 1.3,
+                            bias_std=0.1, n_ignored=0, ignore_values=(-1,),
+                            temperature=(0.5, 1.5), grad="normal", leading=(N,))
+    inp = flp_inputs.make_inputs(w)
+    picks = np.array([V - 1, 768, 896, 767, 895, 999 - 100, 0, 128, 255, 256, V - 2, -1, V, 900])
+    t = picks[np.arange(N) % len(picks)]
+    inp["targets"] = torch.from_numpy(t.astype(np.int64))
+    say(f"case edges: N={N} D={D} V={V} {dtype}, targets cycling through {picks.tolist()}")
+    full_check(inp, to_gpu(inp), dtype)
+
+
 def test_small_bf16_fp32_dweight():
     """bf16 inputs with an fp32 d_weight output (one rounding less)."""
     inp = small_inputs(SMALL[0], 0)
