@@ -332,7 +332,9 @@ struct Engine {
                                              int64_t a_ks, int64_t a_rows_valid, const char* b,
                                              int64_t ldb, int64_t b_ks, int64_t b_rows_valid,
                                              int64_t kbytes, u32x4* smem) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // Wave-uniform, so that the LDS destinations of the direct loads (M0) are scalar.
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave % WM, wn = wave / WM, i = lane & 15, g = lane >> 4;
     const int nsteps = int(kbytes / kStageBytes);
     const int nst = (nsteps + 1) / 2;
