@@ -132,3 +132,25 @@ def test_fp16_row_subsets():
         say(f"  fp16 subset n={n}")
         assert torch.equal(lp, logp[idx]) and torch.equal(ls, lse[idx])
         assert torch.equal(dhs, dh[idx])
+
+
+def test_bf16_rounding_of_denormal_dweight():
+    """The bf16 outputs are rounded to nearest even with denormals kept: with grad_out
+    scaled to 1e-36, dz and d_weight fall in the denormal range, and the bf16 d_weight
+    is still bit for bit the round-to-nearest-even of the fp32 d_weight of the same
+    accumulation (the conversion done on the CPU by torch)."""
+    w = flp_inputs.Workload("denormal_dw", 310, 64, 256, 4096, BF16, w_std=0.05,
+                            bias_std=0.1, n_ignored=2, ignore_values=(-1,),
+                            temperature=None, grad="normal", leading=(64,))
+    g = to_gpu(flp_inputs.make_inputs(w))
+    g["grad_out"] = g["grad_out"] * 1e-36
+    say("case denormal_dw: N=64 D=256 V=4096 bf16, grad_out x 1e-36")
+    _, lse = gpu_forward(g)
+    _, dw16, _ = gpu_backward(g, lse, need_bias=False)
+    _, dw32, _ = gpu_backward(g, lse, need_bias=False, dw_dtype=torch.float32)
+    f = dw32.cpu()
+    tiny = torch.finfo(torch.float32).tiny
+    n_den = int(((f != 0) & (f.abs() < tiny)).sum())
+    say(f"  fp32 d_weight entries in the denormal range: {n_den} of {f.numel()}")
+    assert n_den > 1000
+    assert torch.equal(f.to(BF16), dw16.cpu())
