@@ -9,7 +9,10 @@ the oracle (its test file) must hold for the GPU results.
 - Adding a constant to every bias entry leaves logp unchanged and shifts lse.
 - The gradients are linear in grad_out: scaling it by 2 is exact in every
   floating-point format here, so the gradients double bit for bit; grad_out = 0
-  gives exactly zero gradients."""
+  gives exactly zero gradients.
+- A power-of-two temperature equals scaling W and b, bit for bit (the temperature
+  divides the whole logit).
+- A row's LSE does not depend on its target."""
 import math
 
 import numpy as np
@@ -102,3 +105,43 @@ def test_gradients_linear_in_grad_out(dtype):
     scale = float(db1.abs().sum())
     assert abs(float(db1.double().sum())) <= 1e-4 * max(scale, 1.0)
     np.testing.assert_array_equal(np.isfinite(dh1.float().cpu().numpy()), True)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, BF16])
+def test_power_of_two_temperature_scales_the_whole_logit(dtype):
+    """T = 2^k: dividing (h W^T + b) by T equals scaling W and b by 2^-k, bit for bit,
+    because a power-of-two scaling commutes with every rounding (no value here comes
+    near the under- or overflow range).  This pins the reading that the temperature
+    divides the whole logit, bias included."""
+    inp = _inputs(dtype, temperature=None)
+    g = to_gpu(inp)
+    N = inp["workload"].N
+    k = 2
+    g1 = dict(g)
+    g1["temperature"] = torch.full((N,), float(2 ** k), device="cuda:0")
+    g2 = dict(g)
+    g2["weight"] = g["weight"] * (2.0 ** -k)
+    g2["bias"] = g["bias"] * (2.0 ** -k)
+    say(f"case temperature 2^{k}: {dtype}")
+    logp1, lse1 = gpu_forward(g1)
+    logp2, lse2 = gpu_forward(g2)
+    assert torch.equal(logp1, logp2)
+    assert torch.equal(lse1, lse2)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, BF16])
+def test_lse_does_not_depend_on_the_target(dtype):
+    """A row's LSE is the same bits whatever its target, ignored targets included."""
+    inp = _inputs(dtype)
+    g = to_gpu(inp)
+    V = inp["workload"].V
+    _, lse0 = gpu_forward(g)
+    g2 = dict(g)
+    t = g["targets"].clone()
+    t[::2] = (t[::2] + 1234) % V
+    t[1::7] = -100
+    t[3::11] = V + 5
+    g2["targets"] = t
+    say(f"case lse vs target: {dtype}")
+    _, lse1 = gpu_forward(g2)
+    assert torch.equal(lse0, lse1)
