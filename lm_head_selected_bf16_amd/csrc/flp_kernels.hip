@@ -920,25 +920,21 @@ __global__ __launch_bounds__(128 * WM) void k_dz(DzArgs p) {
       __syncthreads();
     }
     if (p.dzT != nullptr) {
-      // Column-major tile.  Lanes i and i ^ 1 hold adjacent tokens; after swapping
-      // two values, the even lane writes columns c, c+1 and the odd lane columns
-      // c+2, c+3, each as one 4-byte (token, token + 1) pair.
-      const bool even = (i & 1) == 0;
+      // Column-major tile: every lane writes its four values as 2-byte entries of
+      // four column rows (no exchange between lanes).
 #pragma unroll
       for (int mb = 0; mb < WMB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < WNB; ++nb) {
           const f32x4_t d = acc[mb][nb];
-          const float x0 = even ? d[2] : d[0];
-          const float x1 = even ? d[3] : d[1];
-          const float y0 = lane_xor(x0, 1);
-          const float y1 = lane_xor(x1, 1);
-          const int te = wm * RW + mb * 16 + (i & ~1);  // even token of the pair
-          const int c = wn * kHalfCols + nb * 16 + 4 * g + (even ? 0 : 2);
-          const float lo0 = even ? d[0] : y0, hi0 = even ? y0 : d[2];
-          const float lo1 = even ? d[1] : y1, hi1 = even ? y1 : d[3];
-          *reinterpret_cast<uint32_t*>(lds + c * kRowB + te * 2) = pack2<E>(lo0, hi0);
-          *reinterpret_cast<uint32_t*>(lds + (c + 1) * kRowB + te * 2) = pack2<E>(lo1, hi1);
+          const int tk = wm * RW + mb * 16 + i;
+          const int c = wn * kHalfCols + nb * 16 + 4 * g;
+          const uint32_t p01 = pack2<E>(d[0], d[1]), p23 = pack2<E>(d[2], d[3]);
+          uint16_t* col = reinterpret_cast<uint16_t*>(lds + c * kRowB + tk * 2);
+          col[0] = uint16_t(p01);
+          col[kRowB / 2] = uint16_t(p01 >> 16);
+          col[kRowB] = uint16_t(p23);
+          col[3 * (kRowB / 2)] = uint16_t(p23 >> 16);
         }
       __syncthreads();
       for (int idx = tid; idx < kChunks; idx += NT) {
