@@ -280,9 +280,6 @@ flp_status flp_backward(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
   const size_t ts = dtype_size(t_dtype);
   void* dz = d_hidden ? at(workspace, L.dz_off) : nullptr;
   void* wT = d_hidden ? at(workspace, L.wt_off) : nullptr;
-  if (d_hidden &&
-      launch_transpose(x_dtype, weight, V, L.ldz, D, D, wT, s) != hipSuccess)
-    return FLP_HIP_ERROR;
   void* dzT = d_weight ? at(workspace, L.dzt_off) : nullptr;
   void* hT = d_weight ? at(workspace, L.ht_off) : nullptr;
   float* dbp = d_bias ? reinterpret_cast<float*>(at(workspace, L.dbp_off)) : nullptr;
@@ -317,6 +314,11 @@ flp_status flp_backward(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
     z.dbias_part = dbp;
     if (launch_dz(x_dtype, z, s) != hipSuccess) return FLP_HIP_ERROR;
     if (d_hidden) {
+      // W^T is made once, after the first dlogits: that kernel re-reads hidden, which
+      // the forward left in the Infinity Cache and streaming 1.4 GB of W and W^T
+      // through it first would evict.
+      if (c == 0 && launch_transpose(x_dtype, weight, V, L.ldz, D, D, wT, s) != hipSuccess)
+        return FLP_HIP_ERROR;
       GemmArgs g;
       g.a = dz;
       g.b = wT;
