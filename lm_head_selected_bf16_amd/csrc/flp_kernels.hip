@@ -1022,6 +1022,38 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(GemmArgs p) {
                            p.a_ks, p.M - m0, reinterpret_cast<const char*>(p.b) + n0 * p.ldb_b,
                            p.ldb_b, p.b_ks, p.N - n0, p.K * E::kSize, smem);
 
+  if constexpr (STORE == 0 && E::kSize == 2) {
+    // 16-bit output: the tile is staged in the operand ring (rows of BN values plus 16
+    // bytes) and written as 16-byte chunks of whole output rows.  The output is
+    // 16-byte aligned, its row stride (D elements) a multiple of 32 and N = D a
+    // multiple of 8, so every chunk lies inside one row.
+    constexpr int kRowB = BN * 2 + 16;
+    constexpr int kCh = BN * 2 / 16;  // 16-byte chunks per tile row
+    static_assert(size_t(BM) * kRowB <= Eng::kLds, "the staged tile fits the operand ring");
+    char* lds = reinterpret_cast<char*>(smem);
+    __syncthreads();  // every wave is done reading the operand ring
+#pragma unroll
+    for (int mb = 0; mb < WMB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < WNB; ++nb) {
+        const int rl = wm * RW + mb * 16 + i;
+        const int cl = wn * CW + nb * 16 + 4 * g;
+        u32x2 w;
+        w.x = pack2<E>(acc[mb][nb][0], acc[mb][nb][1]);
+        w.y = pack2<E>(acc[mb][nb][2], acc[mb][nb][3]);
+        *reinterpret_cast<u32x2*>(lds + rl * kRowB + cl * 2) = w;
+      }
+    __syncthreads();
+    for (int idx = tid; idx < BM * kCh; idx += Eng::NT) {
+      const int rl = idx / kCh, ch = idx - rl * kCh;
+      const int64_t m = m0 + rl, n = n0 + ch * 8;
+      if (m < p.M && n < p.N)
+        *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.out) + m * p.ldo + n) =
+            *reinterpret_cast<const u32x4*>(lds + rl * kRowB + ch * 16);
+    }
+    return;
+  }
+
 #pragma unroll
   for (int mb = 0; mb < WMB; ++mb) {
     const int64_t m = m0 + wm * RW + mb * 16 + i;
