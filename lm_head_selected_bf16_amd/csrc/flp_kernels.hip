@@ -259,13 +259,15 @@ __device__ __forceinline__ void wait_barrier() {
 
 // ---- the MFMA engine -------------------------------------------------------------------------
 //
-// Two LDS buffers of one 128-byte stage each; stage t lives in buffer t % 2 and
-// holds the MFMA steps 2t (chunks 0-3) and 2t + 1 (chunks 4-7).  Every MFMA step
-// multiplies fragments read from LDS during the previous step.  The workgroup
-// synchronises once per stage, between its two steps: stage t + 1 must have
-// landed (its loads were issued one stage earlier) and every wave must be done
-// reading stage t, whose buffer then receives the loads of stage t + 2.
-template <class E, int BM, int BN, int WM, int WN>
+// A ring of NS LDS buffers of one 128-byte stage each (two for the large tiles);
+// stage t lives in buffer t % NS and holds the MFMA steps 2t (chunks 0-3) and
+// 2t + 1 (chunks 4-7).  Every MFMA step multiplies fragments read from LDS during
+// the previous step.  The workgroup synchronises once per stage, between its two
+// steps: stage t + 1 must have landed (its loads were issued NS - 1 stages
+// earlier) and every wave must be done reading stage t, whose buffer then receives
+// the loads of stage t + NS.  Small tiles do little work per stage, so they use a
+// deeper ring to keep enough loads in flight.
+template <class E, int BM, int BN, int WM, int WN, int NS = 2>
 struct Engine {
   static constexpr int NW = WM * WN;
   static constexpr int NT = 64 * NW;
@@ -274,7 +276,8 @@ struct Engine {
   static constexpr int WMB = RW / 16;
   static constexpr int WNB = CW / 16;
   static constexpr int kSlots = (BM + BN) * 8;  // 16-byte LDS chunks per stage
-  static constexpr size_t kLds = 2 * size_t(kSlots) * 16;
+  static constexpr size_t kLds = NS * size_t(kSlots) * 16;
+  static_assert(NS >= 2, "at least two LDS stages");
   // Loads per stage of the wave that issues the fewest: waiting until at most
   // kLoads are outstanding guarantees, for every wave, that all but its last
   // stage have landed.
@@ -312,7 +315,7 @@ struct Engine {
       __builtin_amdgcn_sched_group_barrier(0x008, kStep, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, kM - kStep * kR, 0);
+    if constexpr (kM > kStep * kR) __builtin_amdgcn_sched_group_barrier(0x008, kM - kStep * kR, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -347,11 +350,15 @@ struct Engine {
     const int fa = (wm * RW + i) * 8 + pos;
     const int fb = (wn * CW + i) * 8 + pos;
     auto issue = [&](int t) {
-      u32x4* dst = smem + (t & 1) * kSlots;
+      u32x4* dst = smem + (t % NS) * kSlots;
       const bool half = ODD && t == nst - 1;
       ta.issue(a, t, half, dst, wave);
       tb.issue(b, t, half, dst + BM * 8, wave);
     };
+    if constexpr (NS > 2) {
+      deep<ODD>(acc, nst, issue, fa, fb, smem);
+      return;
+    }
     issue(0);
     if (nst > 1) {
       issue(1);
@@ -380,6 +387,44 @@ struct Engine {
     };
     const int nfull = ODD ? nst - 1 : nst;
     for (int t = 0; t < nfull; ++t) stage(t);
+    if constexpr (ODD) mmas(acc, f0);
+  }
+
+  // The ring of NS > 2 stages: the first NS stages are issued up front; at the
+  // barrier of stage t, stages t + 2 .. t + NS - 1 may still be in flight (every
+  // stage issues the same number of loads per wave, a half stage included), and
+  // near the end of the K walk everything is waited for.
+  static_assert(NS == 2 || (NS - 1) * (DTile<BM, NW>::kPer + DTile<BN, NW>::kPer) <= 63,
+                "the loads in flight must fit the vmcnt counter");
+  template <bool ODD, class Issue>
+  __device__ __forceinline__ static void deep(f32x4_t (&acc)[WMB][WNB], int nst, Issue& issue,
+                                              int fa, int fb, u32x4* smem) {
+    for (int t = 0; t < NS && t < nst; ++t) issue(t);
+    if (nst >= NS)
+      wait_barrier<(NS - 1) * kLoads>();
+    else
+      wait_barrier<0>();
+    Frag f0, f1;
+    read(f0, smem, fa, fb);
+    int cur = 0;  // buffer of stage t
+    const int nfull = ODD ? nst - 1 : nst;
+    for (int t = 0; t < nfull; ++t) {
+      const int nxt = cur + 1 == NS ? 0 : cur + 1;
+      read(f1, smem + cur * kSlots, fa ^ 4, fb ^ 4);
+      mmas(acc, f0);
+      interleave();
+      if (t + 1 < nst) {
+        if (t + NS - 1 < nst)
+          wait_barrier<(NS - 2) * kLoads>();
+        else
+          wait_barrier<0>();
+        if (t + NS < nst) issue(t + NS);
+      }
+      read(f0, smem + nxt * kSlots, fa, fb);
+      mmas(acc, f1);
+      interleave();
+      cur = nxt;
+    }
     if constexpr (ODD) mmas(acc, f0);
   }
 };
@@ -993,9 +1038,9 @@ __global__ __launch_bounds__(128 * WM) void k_dz(DzArgs p) {
 //   d_weight: M = V, N = D, K = tokens (padded); A = dz^T, B = hidden^T.
 // LOAD: start from the fp32 accumulator p.acc; STORE: 0 = element type to p.out,
 // 1 = fp32 to p.acc.
-template <class E, int BM, int BN, int WM, int WN, bool LOAD, int STORE>
+template <class E, int BM, int BN, int WM, int WN, bool LOAD, int STORE, int NS = 2>
 __global__ __launch_bounds__(64 * WM * WN) void k_gemm(GemmArgs p) {
-  using Eng = Engine<E, BM, BN, WM, WN>;
+  using Eng = Engine<E, BM, BN, WM, WN, NS>;
   constexpr int RW = Eng::RW, CW = Eng::CW, WMB = Eng::WMB, WNB = Eng::WNB;
   extern __shared__ u32x4 smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1195,29 +1240,44 @@ hipError_t dz_cfg(const DzArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <class E, int BM, int BN, int WM, int WN, bool LOAD, int STORE>
+template <class E, int BM, int BN, int WM, int WN, bool LOAD, int STORE, int NS = 2>
 hipError_t gemm_cfg(const GemmArgs& a, hipStream_t s) {
-  using Eng = Engine<E, BM, BN, WM, WN>;
+  using Eng = Engine<E, BM, BN, WM, WN, NS>;
   static std::atomic<int> ready[kMaxDevices];
-  const hipError_t e = prepare(k_gemm<E, BM, BN, WM, WN, LOAD, STORE>, Eng::kLds, ready);
+  const hipError_t e = prepare(k_gemm<E, BM, BN, WM, WN, LOAD, STORE, NS>, Eng::kLds, ready);
   if (e != hipSuccess) return e;
   const int64_t blocks = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  hipLaunchKernelGGL((k_gemm<E, BM, BN, WM, WN, LOAD, STORE>), dim3(unsigned(blocks)),
+  hipLaunchKernelGGL((k_gemm<E, BM, BN, WM, WN, LOAD, STORE, NS>), dim3(unsigned(blocks)),
                      dim3(Eng::NT), Eng::kLds, s, a);
   return hipGetLastError();
 }
 
 // The per-element MFMA chain does not depend on the tile shape, so the GEMM
 // variants may use different tiles and still give the same bits.
+//
+// d_hidden walks the whole vocabulary for every tile and cannot split K without
+// changing the bits, so a batch of few rows has few tiles: there the tiles shrink
+// (more workgroups stream W^T side by side) and the LDS ring deepens.  Thresholds
+// measured on the 16-bit training shape (D = 2688, V = 131072): 64 x 16 tiles are
+// fastest up to 64 rows, 64 x 32 up to 128, 128 x 64 up to 512, 128 x 128 up to
+// 1024, and the 256 x 224 tile from 2048 rows on.
+template <class E>
+hipError_t dx_tiles16(const GemmArgs& a, hipStream_t s) {
+  if (a.M <= 64) return gemm_cfg<E, 64, 16, 4, 1, false, 0, 8>(a, s);
+  if (a.M <= 128) return gemm_cfg<E, 64, 32, 4, 1, false, 0, 8>(a, s);
+  if (a.M <= 512) return gemm_cfg<E, 128, 64, 2, 2, false, 0, 4>(a, s);
+  if (a.M <= 1024) return gemm_cfg<E, 128, 128, 2, 2, false, 0, 3>(a, s);
+  return gemm_cfg<E, 256, 224, 4, 2, false, 0>(a, s);
+}
 template <class E>
 hipError_t dx_dispatch(const GemmArgs& a, hipStream_t s);
 template <>
 hipError_t dx_dispatch<BF16>(const GemmArgs& a, hipStream_t s) {
-  return gemm_cfg<BF16, 256, 224, 4, 2, false, 0>(a, s);
+  return dx_tiles16<BF16>(a, s);
 }
 template <>
 hipError_t dx_dispatch<F16>(const GemmArgs& a, hipStream_t s) {
-  return gemm_cfg<F16, 256, 224, 4, 2, false, 0>(a, s);
+  return dx_tiles16<F16>(a, s);
 }
 template <>
 hipError_t dx_dispatch<F32>(const GemmArgs& a, hipStream_t s) {
@@ -1348,10 +1408,12 @@ hipError_t launch_dbias_fold(const float* part, int64_t n_parts, int64_t ldz, in
 }
 
 const char* kernel_ids() {
-  return "engine: direct global->LDS (buffer_load_dwordx4 lds, whole lines), 2 LDS stages x 128 B of K, "
+  return "engine: direct global->LDS (buffer_load_dwordx4 lds, whole lines), 2 LDS stages x 128 B of K "
+         "(3-8 for the small dX tiles), "
          "mfma_f32_16x16x32_bf16 | 16x16x32_f16 | 16x16x4f32; k_fwd<BM 32/64/128 x BN 256 2x2 waves, "
          "BM 256 4x2 waves>; k_merge<8 rows x 32 segments>; k_dz<BM 256 x BN 256, 4x2 waves>; "
-         "k_gemm dX, dW<256x224, 4x2 waves, K-blocked operands>; k_transpose (K-blocked); "
+         "k_gemm dX, dW<256x224, 4x2 waves, K-blocked operands; dX for <= 1024 rows: 64x16, "
+         "64x32, 128x64, 128x128>; k_transpose (K-blocked); "
          "k_dbias_fold; k_fill; k_logits_fwd, k_logits_bwd<one wave per row>; "
          "rows: k_mark, k_compact, k_gather, k_scatter_rows, k_scatter_hidden; "
          "embedding: k_embed_fwd, radix sort (k_sort_init, k_sort_hist, k_sort_scatter; zero-row "

@@ -77,8 +77,11 @@ def train_small():
     return inp, g, logp, lse
 
 
-@pytest.mark.parametrize("n", [1, 7, 64, 257])
+@pytest.mark.parametrize("n", [1, 7, 64, 100, 257, 700])
 def test_d_hidden_row_subsets(train_small, n):
+    """d_hidden of a row does not depend on the batch: the subsets take every d_hidden
+    tile shape (64 x 16, 64 x 32, 128 x 64, 128 x 128) against the full batch's
+    256 x 224 tiles."""
     inp, g, logp, lse = train_small
     dh, _, _ = gpu_backward(g, lse, need_weight=False, need_bias=False)
     rows = flp_inputs.random_rows(1100, n, seed=2000 + n).numpy()
