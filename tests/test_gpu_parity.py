@@ -64,6 +64,10 @@ SMALL = [
     # an odd number of 128-byte K stages (D = 192: three), so that the last stage's
     # fragments come from LDS buffer 0, the one the forward epilogue reuses
     (BF16, 200, 192, 1500, 0.1, (0.5, 1.5), torch.int64, 3),
+    # d_hidden column tiles only partly inside D: 128 x 64 tiles over D = 96 and
+    # 128 x 128 tiles over D = 160
+    (BF16, 150, 96, 1000, 0.1, (0.5, 1.5), torch.int64, 3),
+    (BF16, 600, 160, 777, None, None, torch.int64, 4),
     # the smallest shapes the gates allow: D = 32 (a single half K stage), V = 1
     (BF16, 50, 32, 700, 0.1, None, torch.int64, 2),
     (BF16, 33, 64, 1, 0.1, (0.5, 1.5), torch.int64, 2),
