@@ -56,7 +56,9 @@ typedef enum flp_status {
   FLP_OK = 0,
   FLP_INVALID_ARGUMENT = 1,      /* null required pointer, N < 0, V < 1, D < 1, overlap */
   FLP_UNSUPPORTED_DTYPE = 2,     /* a dtype outside the lists below */
-  FLP_UNSUPPORTED_SHAPE = 3,     /* D % 32 != 0, or a size beyond the 64-bit index range */
+  FLP_UNSUPPORTED_SHAPE = 3,     /* D % 32 != 0, 256 * D * element size >= 2^31 (32-bit row
+                                    offsets inside a 256-row tile), or a size beyond the
+                                    64-bit index range */
   FLP_MISALIGNED = 4,            /* hidden/weight/workspace not 16-byte aligned, others not
                                     aligned to their element size */
   FLP_WORKSPACE_TOO_SMALL = 5,   /* workspace_bytes below the *_workspace_bytes minimum */
@@ -75,6 +77,11 @@ typedef enum flp_dtype {
 /*
  * Forward workspace in bytes for (N, D, V): per-row, per-vocabulary-tile
  * partial (max, sum-of-exp) pairs and the target logits.  16-byte aligned.
+ * These are the per-row softmax statistics of each vocabulary slab that the
+ * "Fused Linear LogP" docs page folds instead of materialising the logits
+ * (intro and "Tensor Parallel Vocab Shards": per-slab partials combined in a
+ * fixed order); the caller provides the memory so that the library allocates
+ * nothing.  Returns 0 for N < 0, D < 1 or V < 1.
  */
 size_t flp_forward_workspace_bytes(int64_t N, int64_t D, int64_t V);
 
@@ -188,7 +195,12 @@ flp_status flp_logits_backward(int64_t N, int64_t V, flp_dtype x_dtype, const fl
                                flp_dtype t_dtype, void* d_logits, void* stream);
 
 /*
- * Backward workspace in bytes.  chunk_rows = 0 asks for the minimum (row
+ * Backward workspace in bytes: the dlogits tile buffers the backward keeps
+ * between its recompute and its two GEMMs ("Fused Linear LogP" docs page,
+ * intro: tiled dlogits workspaces), the transposed operands, the d_bias
+ * partials and, when the rows run in several chunks, the fp32 d_weight
+ * accumulator that makes the chunking bit-neutral (PR #555 summary bullets:
+ * chunked deterministic backward).  chunk_rows = 0 asks for the minimum (row
  * chunks of 256, or one chunk of the whole batch when that needs less because a
  * single chunk needs no fp32 d_W accumulator); a positive chunk_rows asks for the size that lets the
  * backward process that many rows per chunk (rounded up to a multiple of
@@ -387,10 +399,21 @@ void flp_profile_enable(int on);
  * event query fails. */
 flp_status flp_profile_read(double* ms, int64_t* count, int n);
 
-/* Static text for a status code. */
+/*
+ * Static text for a status code.  Every unsupported case is reported as an
+ * error, never served by another path: the fail-closed gates of PR #555
+ * (summary bullets and "Acceptance checks").  Unknown codes give
+ * "FLP_UNKNOWN_STATUS".  The string is owned by the library.
+ */
 const char* flp_status_string(flp_status status);
 
-/* Build provenance: library version, target, kernel ids and tile shapes. */
+/*
+ * Build provenance: library version, target architecture, git revision and the
+ * kernel ids and tile shapes, plus "fallback=none" (this library has no
+ * fallback path).  PR #555 (summary bullets, "Acceptance checks") records which
+ * backend and kernels produced a result and that no fallback ran; this string
+ * is that record for this library.  Static storage owned by the library.
+ */
 const char* flp_build_info(void);
 
 #ifdef __cplusplus

@@ -18,7 +18,9 @@ using namespace flp;
 // Per-device cache of "is gfx950": 0 = unknown, 1 = yes, 2 = no.
 std::atomic<int> g_arch[64];
 
-flp_status check_device() {
+}  // namespace
+
+flp_status flp::check_device() {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FLP_UNSUPPORTED_DEVICE;
   if (dev < 64) {
@@ -32,6 +34,8 @@ flp_status check_device() {
   if (dev < 64) g_arch[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
   return ok ? FLP_OK : FLP_UNSUPPORTED_DEVICE;
 }
+
+namespace {
 
 inline char* at(void* base, size_t off) { return static_cast<char*>(base) + off; }
 
@@ -92,24 +96,10 @@ ProfScope::~ProfScope() {
   g_prof_recs.push_back(ProfRec{kind, a, b});
 }
 
-}  // namespace flp
-
-extern "C" {
-
-size_t flp_forward_workspace_bytes(int64_t N, int64_t D, int64_t V) {
-  if (N < 0 || D < 1 || V < 1) return 0;
-  return fwd_layout(N, D, V).total;
-}
-
-flp_status flp_forward(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype, const void* hidden,
-                       const void* weight, const float* bias, const void* targets,
-                       flp_dtype t_dtype, const float* temperature, float* out_logp,
-                       float* out_lse, void* workspace, size_t workspace_bytes, void* stream) {
-  flp_status st = validate_forward(N, D, V, x_dtype, hidden, weight, bias, targets, t_dtype,
-                                   temperature, out_logp, out_lse, workspace, workspace_bytes);
-  if (st != FLP_OK || N == 0) return st;
-  if ((st = check_device()) != FLP_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+flp_status enqueue_forward(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype, const void* hidden,
+                           const void* weight, const float* bias, const void* targets,
+                           flp_dtype t_dtype, const float* temperature, float* out_logp,
+                           float* out_lse, void* workspace, hipStream_t s) {
   const FwdLayout L = fwd_layout(N, D, V);
   FwdArgs f;
   f.hidden = hidden;
@@ -137,6 +127,27 @@ flp_status flp_forward(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype, const
   m.lse = out_lse;
   if (launch_merge(m, s) != hipSuccess) return FLP_HIP_ERROR;
   return FLP_OK;
+}
+
+}  // namespace flp
+
+extern "C" {
+
+size_t flp_forward_workspace_bytes(int64_t N, int64_t D, int64_t V) {
+  if (N < 0 || D < 1 || V < 1) return 0;
+  return fwd_layout(N, D, V).total;
+}
+
+flp_status flp_forward(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype, const void* hidden,
+                       const void* weight, const float* bias, const void* targets,
+                       flp_dtype t_dtype, const float* temperature, float* out_logp,
+                       float* out_lse, void* workspace, size_t workspace_bytes, void* stream) {
+  flp_status st = validate_forward(N, D, V, x_dtype, hidden, weight, bias, targets, t_dtype,
+                                   temperature, out_logp, out_lse, workspace, workspace_bytes);
+  if (st != FLP_OK || N == 0) return st;
+  if ((st = check_device()) != FLP_OK) return st;
+  return enqueue_forward(N, D, V, x_dtype, hidden, weight, bias, targets, t_dtype, temperature,
+                         out_logp, out_lse, workspace, static_cast<hipStream_t>(stream));
 }
 
 size_t flp_forward_partial_bytes(int64_t N, int64_t V_local) {
@@ -663,7 +674,9 @@ const char* flp_status_string(flp_status status) {
     case FLP_OK: return "FLP_OK";
     case FLP_INVALID_ARGUMENT: return "FLP_INVALID_ARGUMENT: null pointer, negative size or overlapping buffers";
     case FLP_UNSUPPORTED_DTYPE: return "FLP_UNSUPPORTED_DTYPE";
-    case FLP_UNSUPPORTED_SHAPE: return "FLP_UNSUPPORTED_SHAPE: D must be a multiple of 32";
+    case FLP_UNSUPPORTED_SHAPE:
+      return "FLP_UNSUPPORTED_SHAPE: D must be a multiple of 32 with 256 * D * element size < 2^31, "
+             "and sizes must fit the index range";
     case FLP_MISALIGNED: return "FLP_MISALIGNED";
     case FLP_WORKSPACE_TOO_SMALL: return "FLP_WORKSPACE_TOO_SMALL";
     case FLP_UNSUPPORTED_DEVICE: return "FLP_UNSUPPORTED_DEVICE: needs gfx950 (MI355X)";
@@ -675,7 +688,8 @@ const char* flp_status_string(flp_status status) {
 const char* flp_build_info(void) {
   static const std::string info = [] {
     char buf[1024];
-    std::snprintf(buf, sizeof(buf), "flp 0.1 gfx950 vocab_tile=%lld row_quantum=%lld git=%s | %s",
+    std::snprintf(buf, sizeof(buf),
+                  "flp 0.2 gfx950 fallback=none vocab_tile=%lld row_quantum=%lld git=%s | %s",
                   (long long)kVocabTile, (long long)kRowQuantum,
 #ifdef FLP_GIT_HASH
                   FLP_GIT_HASH,

@@ -209,8 +209,10 @@ struct DTile {
   static constexpr int kInsts = ROWS / 8;
   static constexpr int kPer = (kInsts + NW - 1) / NW;
   // Wave w issues instructions w*kPer .. min(kInsts, (w+1)*kPer) - 1, so the last
-  // waves may issue fewer; kMin is the fewest any wave issues per stage.
-  static constexpr int kMin = kInsts - (NW - 1) * kPer > 0 ? kInsts - (NW - 1) * kPer : 0;
+  // waves may issue fewer: count(w) per stage.
+  static constexpr int count(int w) {
+    return kInsts - w * kPer <= 0 ? 0 : (kInsts - w * kPer > kPer ? kPer : kInsts - w * kPer);
+  }
   static_assert(ROWS % 16 == 0, "tile rows must be a multiple of 16");
   int q;                // row within the instruction's 8 rows
   int c0, c1;           // logical chunk loaded by this lane for even / odd instructions
@@ -256,6 +258,11 @@ template <int N>
 __device__ __forceinline__ void wait_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
+template <int N>
+__device__ __forceinline__ void wait_own() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
 
 // ---- the MFMA engine -------------------------------------------------------------------------
 //
@@ -278,10 +285,6 @@ struct Engine {
   static constexpr int kSlots = (BM + BN) * 8;  // 16-byte LDS chunks per stage
   static constexpr size_t kLds = NS * size_t(kSlots) * 16;
   static_assert(NS >= 2, "at least two LDS stages");
-  // Loads per stage of the wave that issues the fewest: waiting until at most
-  // kLoads are outstanding guarantees, for every wave, that all but its last
-  // stage have landed.
-  static constexpr int kLoads = DTile<BM, NW>::kMin + DTile<BN, NW>::kMin;
   static_assert(RW % 16 == 0 && CW % 16 == 0, "wave tile must be a multiple of 16");
 
   struct Frag {
@@ -356,13 +359,14 @@ struct Engine {
       tb.issue(b, t, half, dst + BM * 8, wave);
     };
     if constexpr (NS > 2) {
-      deep<ODD>(acc, nst, issue, fa, fb, smem);
+      deep<ODD>(acc, nst, issue, fa, fb, smem, wave);
       return;
     }
     issue(0);
     if (nst > 1) {
       issue(1);
-      wait_barrier<kLoads>();
+      wait_stages<1>(wave);
+      barrier_only();
     } else {
       wait_barrier<0>();
     }
@@ -393,17 +397,41 @@ struct Engine {
   // The ring of NS > 2 stages: the first NS stages are issued up front; at the
   // barrier of stage t, stages t + 2 .. t + NS - 1 may still be in flight (every
   // stage issues the same number of loads per wave, a half stage included), and
-  // near the end of the K walk everything is waited for.
+  // near the end of the K walk everything is waited for.  Waves may issue
+  // different numbers of loads per stage (the instructions of a tile are split
+  // over the waves in runs of kPer), so each wave waits on its own count: a
+  // wave-uniform branch picks the immediate, and every wave then reaches the one
+  // barrier.
   static_assert(NS == 2 || (NS - 1) * (DTile<BM, NW>::kPer + DTile<BN, NW>::kPer) <= 63,
                 "the loads in flight must fit the vmcnt counter");
+  static constexpr int loads_of(int w) { return DTile<BM, NW>::count(w) + DTile<BN, NW>::count(w); }
+  // Last wave of the run of waves from w on that issue as many loads as wave w.
+  static constexpr int run_end(int w) {
+    return w + 1 < NW && loads_of(w + 1) == loads_of(w) ? run_end(w + 1) : w;
+  }
+  template <int Stages, int W = 0>
+  __device__ __forceinline__ static void wait_stages(int wave) {
+    constexpr int Last = run_end(W);
+    if constexpr (Last + 1 < NW) {
+      if (wave <= Last) {
+        wait_own<Stages * loads_of(W)>();
+        return;
+      }
+      wait_stages<Stages, Last + 1>(wave);
+    } else {
+      wait_own<Stages * loads_of(W)>();
+    }
+  }
   template <bool ODD, class Issue>
   __device__ __forceinline__ static void deep(f32x4_t (&acc)[WMB][WNB], int nst, Issue& issue,
-                                              int fa, int fb, u32x4* smem) {
+                                              int fa, int fb, u32x4* smem, int wave) {
     for (int t = 0; t < NS && t < nst; ++t) issue(t);
-    if (nst >= NS)
-      wait_barrier<(NS - 1) * kLoads>();
-    else
+    if (nst >= NS) {
+      wait_stages<NS - 1>(wave);
+      barrier_only();
+    } else {
       wait_barrier<0>();
+    }
     Frag f0, f1;
     read(f0, smem, fa, fb);
     int cur = 0;  // buffer of stage t
@@ -414,10 +442,12 @@ struct Engine {
       mmas(acc, f0);
       interleave();
       if (t + 1 < nst) {
-        if (t + NS - 1 < nst)
-          wait_barrier<(NS - 2) * kLoads>();
-        else
+        if (t + NS - 1 < nst) {
+          wait_stages<NS - 2>(wave);
+          barrier_only();
+        } else {
           wait_barrier<0>();
+        }
         if (t + NS < nst) issue(t + NS);
       }
       read(f0, smem + nxt * kSlots, fa, fb);

@@ -7,6 +7,17 @@
 
 namespace flp {
 
+// The current device is a gfx950 (cached per device): FLP_OK, else
+// FLP_UNSUPPORTED_DEVICE (or FLP_HIP_ERROR when the device cannot be queried).
+flp_status check_device();
+// Enqueue the forward (logit tiles, then the ascending merge) on `s` with its
+// workspace at `workspace`, laid out as fwd_layout(N, D, V).  The arguments
+// have been validated.
+flp_status enqueue_forward(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype, const void* hidden,
+                           const void* weight, const float* bias, const void* targets,
+                           flp_dtype t_dtype, const float* temperature, float* out_logp,
+                           float* out_lse, void* workspace, hipStream_t s);
+
 struct FwdArgs {
   const void* hidden;
   const void* weight;

@@ -61,6 +61,12 @@ flp_status check_dims(int64_t N, int64_t D, int64_t V, flp_dtype x, flp_dtype t)
   if (x != FLP_BF16 && x != FLP_F16 && x != FLP_F32) return FLP_UNSUPPORTED_DTYPE;
   if (t != FLP_I64 && t != FLP_I32) return FLP_UNSUPPORTED_DTYPE;
   if (D % 32 != 0) return FLP_UNSUPPORTED_SHAPE;
+  // The logit-tile kernels address the rows of a hidden / weight tile through a
+  // buffer resource with 32-bit offsets (row r of at most 256 at r * D * size,
+  // plus the chunk within the 128-byte stage): every such offset must stay below
+  // the resource's 2^31 - 1 records.
+  if (D > kMaxIndex / 256 || D * int64_t(dtype_size(x)) * 256 >= (int64_t(1) << 31))
+    return FLP_UNSUPPORTED_SHAPE;
   const int64_t rows = std::max<int64_t>(round_up(std::max<int64_t>(N, 1), kRowQuantum), 1);
   const int64_t ldz = round_up(V, kVocabTile);
   if (!mul_ok(rows, D) || !mul_ok(ldz, D) || !mul_ok(rows, ldz) ||
@@ -232,16 +238,20 @@ flp_status validate_rows(int64_t N, const void* rows, flp_dtype r, int64_t n_row
   return FLP_OK;
 }
 
-flp_status validate_forward(int64_t N, int64_t D, int64_t V, flp_dtype x, const void* hidden,
-                            const void* weight, const float* bias, const void* targets,
-                            flp_dtype t, const float* temperature, const float* out_logp,
-                            const float* out_lse, const void* workspace,
-                            size_t workspace_bytes) {
+namespace {
+// The forward's gates.  own_scratch: the workspace is the library's own fixed
+// array (the allocation-free entry point), which cannot overlap a caller's
+// buffer, so only its size is checked.
+flp_status forward_gates(int64_t N, int64_t D, int64_t V, flp_dtype x, const void* hidden,
+                         const void* weight, const float* bias, const void* targets, flp_dtype t,
+                         const float* temperature, const float* out_logp, const float* out_lse,
+                         const void* workspace, size_t workspace_bytes, bool own_scratch) {
   flp_status st = check_dims(N, D, V, x, t);
   if (st != FLP_OK) return st;
   if (N == 0) return FLP_OK;
-  if (!hidden || !weight || !targets || !out_logp || !workspace) return FLP_INVALID_ARGUMENT;
-  if (!aligned(hidden, 16) || !aligned(weight, 16) || !aligned(workspace, 16) ||
+  if (!hidden || !weight || !targets || !out_logp || (!own_scratch && !workspace))
+    return FLP_INVALID_ARGUMENT;
+  if (!aligned(hidden, 16) || !aligned(weight, 16) || (!own_scratch && !aligned(workspace, 16)) ||
       !aligned(bias, 4) || !aligned(temperature, 4) || !aligned(out_logp, 4) ||
       !aligned(out_lse, 4) || !aligned(targets, dtype_size(t)))
     return FLP_MISALIGNED;
@@ -250,10 +260,20 @@ flp_status validate_forward(int64_t N, int64_t D, int64_t V, flp_dtype x, const 
                       span(bias, size_t(V) * 4), span(targets, size_t(N) * dtype_size(t)),
                       span(temperature, size_t(N) * 4)};
   const Span outs[] = {span(out_logp, size_t(N) * 4), span(out_lse, size_t(N) * 4),
-                       span(workspace, workspace_bytes)};
+                       own_scratch ? Span() : span(workspace, workspace_bytes)};
   if (any_alias(outs, 3, ins, 5)) return FLP_INVALID_ARGUMENT;
   if (workspace_bytes < fwd_layout(N, D, V).total) return FLP_WORKSPACE_TOO_SMALL;
   return FLP_OK;
+}
+}  // namespace
+
+flp_status validate_forward(int64_t N, int64_t D, int64_t V, flp_dtype x, const void* hidden,
+                            const void* weight, const float* bias, const void* targets,
+                            flp_dtype t, const float* temperature, const float* out_logp,
+                            const float* out_lse, const void* workspace,
+                            size_t workspace_bytes) {
+  return forward_gates(N, D, V, x, hidden, weight, bias, targets, t, temperature, out_logp,
+                       out_lse, workspace, workspace_bytes, false);
 }
 
 flp_status validate_forward_partial(int64_t N, int64_t D, int64_t V_local, int64_t vocab_start,

@@ -37,6 +37,9 @@ def test_status_strings_and_build_info():
         assert abi.flp_status_string(code).startswith(name)
     info = abi.flp_build_info()
     assert "gfx950" in info and "vocab_tile=256" in info
+    # provenance: the library has no fallback path and says so
+    assert "fallback=none" in info
+    assert abi.flp_status_string(99) == "FLP_UNKNOWN_STATUS"
 
 
 # fake, 16-byte aligned, non-overlapping device addresses
@@ -80,6 +83,22 @@ def fwd(**kw):
 ])
 def test_forward_gates(kw, expect):
     assert abi.STATUS_NAMES[fwd(**kw)] == expect
+
+
+@pytest.mark.parametrize("x,esize", [(BF16, 2), (abi.FLP_F16, 2), (F32, 4)])
+def test_hidden_row_offsets_stay_within_32_bits(x, esize):
+    """A logit tile addresses its up to 256 rows with 32-bit offsets r * D * size: the
+    largest D whose 256 rows stay below 2^31 bytes passes the shape gate (the call then
+    stops at the later workspace gate, before any device work), the next multiple of 32
+    is rejected (for the forward, the shard forward and the backward)."""
+    d_max = ((1 << 31) - 1) // (256 * esize) // 32 * 32
+    for D_, expect in ((d_max, "FLP_WORKSPACE_TOO_SMALL"), (d_max + 32, "FLP_UNSUPPORTED_SHAPE")):
+        assert abi.STATUS_NAMES[fwd(N=1, V=1, D=D_, x=x, wsb=16)] == expect, D_
+    assert abi.STATUS_NAMES[fpart(N=1, D=d_max + 32, x=x, VL=256, vs=0, VT=256)] == \
+        "FLP_UNSUPPORTED_SHAPE"
+    # the backward rejects the same D before sizing its workspace
+    assert abi.STATUS_NAMES[bwd(N=1, V=1, D=d_max + 32, x=x, dwt=x, wsb=1 << 40)] == \
+        "FLP_UNSUPPORTED_SHAPE"
 
 
 def fpart(**kw):

@@ -119,15 +119,17 @@ def test_backward_chunking_is_bit_neutral(train_small):
 
 def test_fp16_row_subsets():
     """fp16 inputs take the same kernels with the fp16 MFMA: rows stay bitwise
-    independent of the batch."""
-    w = flp_inputs.Workload("fp16_inv", 300, 1000, 512, 4096, torch.float16, w_std=0.06,
+    independent of the batch.  The full batch (1100 rows) runs d_hidden in 256 x 224
+    tiles, the subsets in each of the small-batch tiles (64 x 16, 64 x 32, 128 x 64,
+    128 x 128)."""
+    w = flp_inputs.Workload("fp16_inv", 300, 1100, 512, 4096, torch.float16, w_std=0.06,
                             bias_std=0.1, n_ignored=4, ignore_values=(-1, 4096),
-                            temperature=(0.5, 1.5), grad="normal", leading=(1000,))
+                            temperature=(0.5, 1.5), grad="normal", leading=(1100,))
     g = to_gpu(flp_inputs.make_inputs(w))
     logp, lse = gpu_forward(g)
     dh, _, _ = gpu_backward(g, lse, need_weight=False, need_bias=False)
-    for n in (1, 7, 257):
-        rows = flp_inputs.random_rows(1000, n, seed=300 + n).numpy()
+    for n in (1, 7, 100, 257, 700):
+        rows = flp_inputs.random_rows(1100, n, seed=300 + n).numpy()
         sub = _subset(g, rows)
         lp, ls = gpu_forward(sub)
         dhs, _, _ = gpu_backward(sub, ls, need_weight=False, need_bias=False)

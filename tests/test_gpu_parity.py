@@ -7,6 +7,8 @@ d_weight / d_bias at full size use a grad_out that is non-zero on sampled rows
 only (every other row then contributes exactly zero), plus properties that hold
 at any size."""
 import dataclasses
+import os
+import time
 
 import numpy as np
 import pytest
@@ -61,6 +63,11 @@ SMALL = [
     # fp16 inputs (the docs page's Tensor Contract: bf16 / fp16 / fp32)
     (torch.float16, 300, 512, 4133, 0.1, (0.5, 1.5), torch.int64, 7),
     (torch.float16, 513, 2688, 2048, 0.1, None, torch.int32, 9),
+    # fp16 through each small-batch d_hidden tile: 64 x 16 (<= 64 rows), 64 x 32
+    # (<= 128), 128 x 64 (<= 512, the 300-row case above), 128 x 128 (<= 1024)
+    (torch.float16, 40, 320, 3000, 0.1, (0.5, 1.5), torch.int64, 3),
+    (torch.float16, 100, 320, 3000, None, None, torch.int32, 4),
+    (torch.float16, 700, 320, 1300, 0.1, (0.5, 1.5), torch.int64, 6),
     # an odd number of 128-byte K stages (D = 192: three), so that the last stage's
     # fragments come from LDS buffer 0, the one the forward epilogue reuses
     (BF16, 200, 192, 1500, 0.1, (0.5, 1.5), torch.int64, 3),
@@ -198,6 +205,43 @@ def _train_like(name, n_sample, ws_bytes=None):
 def test_train_n16384():
     say("case train_n16384: N=16384 D=2688 V=131072 bf16, bias, fwd+bwd")
     _train_like("train_n16384", 32)
+
+
+@pytest.mark.timeout(900)
+def test_train_n16384_dense_grad_every_element():
+    """The training workload with its own dense grad_out ~ N(0, 1): every element of
+    d_weight and d_bias (reduction cell) and of d_hidden, logp and lse (log-prob cell)
+    against the oracle over all 16384 rows, so that the error accumulated over 16384
+    real contributions to each d_weight / d_bias entry is measured (PR #555,
+    "det-GEMM split verification" and "Tolerance").  The oracle takes about a minute
+    on 16 host cores."""
+    say("case train_n16384 dense grad: N=16384 D=2688 V=131072 bf16, bias, every element")
+    inp = inputs("train_n16384")
+    g = to_gpu(inp)
+    logp, lse = gpu_forward(g)
+    dh, dw, db = gpu_backward(g, lse, need_bias=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    rl, rs = oracle_forward(inp)
+    t1 = time.perf_counter()
+    check_close("logp", logp, rl, **LOGP_CELL)
+    check_close("lse", lse, rs, **LOGP_CELL)
+    del rl, rs
+    t2 = time.perf_counter()
+    odh, odw, odb = oracle_backward(inp)
+    t3 = time.perf_counter()
+    say(f"  oracle over all 16384 rows: forward {t1 - t0:.1f} s, backward {t3 - t2:.1f} s "
+        f"({len(os.sched_getaffinity(0))} host cores available)")
+    check_close("d_hidden", dh, odh, **LOGP_CELL)
+    del odh, dh
+    check_close("d_bias", db, odb, **REDUCTION_CELL)
+    # d_weight: 352 M entries, compared in blocks of vocabulary rows
+    worst = 0.0
+    for v0 in range(0, odw.shape[0], 16384):
+        blk = slice(v0, v0 + 16384)
+        worst = max(worst, check_close(f"d_weight[{v0}:{v0 + 16384}]", dw[blk], odw[blk],
+                                       **REDUCTION_CELL))
+    say(f"  d_weight over all rows: max|err| = {worst:.3e}")
 
 
 def test_longseq_n65600_multichunk():
