@@ -113,6 +113,34 @@ flp_status flp_forward(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Largest forward workspace (flp_forward_workspace_bytes) that the
+ * allocation-free forward serves: the size of its fixed per-device scratch
+ * array, 33 MiB (at V = 131072, batches of up to 8439 rows).
+ */
+#define FLP_FORWARD_NOALLOC_MAX_BYTES ((size_t)33 << 20)
+
+/*
+ * Allocation-free forward, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The same computation as flp_forward, with the same bits, but the
+ * workspace is a fixed array of FLP_FORWARD_NOALLOC_MAX_BYTES that the library
+ * holds on every device it runs on (from the first call on that device until
+ * the process ends); the caller passes only inputs and outputs.  The call
+ * allocates nothing: no hipMalloc, no hipFree, no allocating library routine
+ * (keep the optional kernel timing below off, since it creates HIP events).
+ *
+ * Arguments, gates and statuses as for flp_forward, plus FLP_WORKSPACE_TOO_SMALL
+ * when flp_forward_workspace_bytes(N, D, V) exceeds FLP_FORWARD_NOALLOC_MAX_BYTES.
+ * All calls on one device share its array: calls that overlap in time on one
+ * device (two streams, two threads) race and must be serialised by the caller.
+ */
+flp_status flp_forward_noalloc(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
+                               const void* hidden, const void* weight, const float* bias,
+                               const void* targets, flp_dtype t_dtype,
+                               const float* temperature, float* out_logp, float* out_lse,
+                               void* stream);
+
+/*
  * Vocabulary shards ("Fused Linear LogP" docs page, "Tensor Parallel Vocab
  * Shards"): a rank that holds rows [vocab_start, vocab_start + V_local) of the
  * weight computes the per-tile partials of its slice; the partials of all

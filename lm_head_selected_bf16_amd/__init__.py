@@ -19,7 +19,7 @@ from ._abi import (FLP_BF16, FLP_F16, FLP_F32, FLP_I32, FLP_I64, FLP_OK, FlpErro
                    flp_backward_indexed_workspace_bytes,
                    flp_backward_workspace_bytes, flp_build_info, flp_embedding_backward,
                    flp_embedding_backward_workspace_bytes, flp_embedding_forward, flp_forward,
-                   flp_forward_indexed,
+                   flp_forward_indexed, flp_forward_noalloc, FLP_FORWARD_NOALLOC_MAX_BYTES,
                    flp_forward_indexed_workspace_bytes, flp_forward_partial,
                    flp_forward_partial_bytes, flp_forward_workspace_bytes, flp_logits_backward,
                    flp_logits_backward_indexed, flp_logits_forward, flp_logits_forward_indexed,
@@ -37,6 +37,7 @@ from .torch_ops import (LinearLogp, backward, backward_workspace_bytes,  # noqa:
 __all__ = [
     "FLP_BF16", "FLP_F16", "FLP_F32", "FLP_I32", "FLP_I64", "FLP_OK", "FlpError",
     "flp_forward", "flp_backward", "flp_forward_workspace_bytes", "flp_backward_workspace_bytes",
+    "flp_forward_noalloc", "FLP_FORWARD_NOALLOC_MAX_BYTES",
     "flp_backward_chunk_rows",
     "flp_forward_partial", "flp_forward_partial_bytes", "flp_merge",
     "flp_logits_forward", "flp_logits_backward",

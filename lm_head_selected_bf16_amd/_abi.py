@@ -33,6 +33,8 @@ SIGNATURES = {
     "flp_forward_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "flp_forward": (_int, [_i64, _i64, _i64, _int, _vp, _vp, _fp, _vp, _int, _fp, _fp, _fp, _vp,
                            _sz, _vp]),
+    "flp_forward_noalloc": (_int, [_i64, _i64, _i64, _int, _vp, _vp, _fp, _vp, _int, _fp, _fp, _fp,
+                                   _vp]),
     "flp_forward_partial_bytes": (_sz, [_i64, _i64]),
     "flp_forward_partial": (_int, [_i64, _i64, _i64, _i64, _i64, _int, _vp, _vp, _fp, _vp, _int, _fp,
                                    _vp, _fp, _vp]),
@@ -107,6 +109,17 @@ def status_string(status: int) -> str:
 
 def flp_forward_workspace_bytes(N: int, D: int, V: int) -> int:
     return int(load().flp_forward_workspace_bytes(N, D, V))
+
+
+# Size of the allocation-free forward's fixed per-device scratch array (FLP_FORWARD_NOALLOC_MAX_BYTES).
+FLP_FORWARD_NOALLOC_MAX_BYTES = 33 << 20
+
+
+def flp_forward_noalloc(N, D, V, x_dtype, hidden, weight, bias, targets, t_dtype, temperature,
+                        out_logp, out_lse, stream) -> int:
+    """Raw call: every pointer argument is an int address (0 for NULL)."""
+    return int(load().flp_forward_noalloc(N, D, V, x_dtype, hidden, weight, bias, targets, t_dtype,
+                                          temperature, out_logp, out_lse, stream))
 
 
 def flp_forward_partial_bytes(N: int, V_local: int) -> int:

@@ -17,7 +17,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libflp.so")
-SOURCES = ["flp_kernels.hip", "flp_rows.hip", "flp_embed.hip", "flp_probe.hip", "flp_api.cpp", "flp_plan.cpp"]
+SOURCES = ["flp_kernels.hip", "flp_rows.hip", "flp_embed.hip", "flp_probe.hip", "flp_noalloc.hip",
+           "flp_api.cpp", "flp_plan.cpp"]
 
 
 def _hipcc() -> str:

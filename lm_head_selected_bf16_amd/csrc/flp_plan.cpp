@@ -276,6 +276,15 @@ flp_status validate_forward(int64_t N, int64_t D, int64_t V, flp_dtype x, const 
                        out_lse, workspace, workspace_bytes, false);
 }
 
+flp_status validate_forward_noalloc(int64_t N, int64_t D, int64_t V, flp_dtype x,
+                                    const void* hidden, const void* weight, const float* bias,
+                                    const void* targets, flp_dtype t, const float* temperature,
+                                    const float* out_logp, const float* out_lse,
+                                    size_t scratch_bytes) {
+  return forward_gates(N, D, V, x, hidden, weight, bias, targets, t, temperature, out_logp,
+                       out_lse, nullptr, scratch_bytes, true);
+}
+
 flp_status validate_forward_partial(int64_t N, int64_t D, int64_t V_local, int64_t vocab_start,
                                     int64_t V_total, flp_dtype x, const void* hidden,
                                     const void* weight, const float* bias, const void* targets,

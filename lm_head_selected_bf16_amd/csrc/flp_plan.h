@@ -106,6 +106,13 @@ flp_status validate_forward(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
                             const void* targets, flp_dtype t_dtype, const float* temperature,
                             const float* out_logp, const float* out_lse,
                             const void* workspace, size_t workspace_bytes);
+// The allocation-free forward: the forward's gates on everything the caller passes,
+// and its workspace size against the library's fixed scratch array.
+flp_status validate_forward_noalloc(int64_t N, int64_t D, int64_t V, flp_dtype x_dtype,
+                                    const void* hidden, const void* weight, const float* bias,
+                                    const void* targets, flp_dtype t_dtype,
+                                    const float* temperature, const float* out_logp,
+                                    const float* out_lse, size_t scratch_bytes);
 // Vocabulary-shard forward and the merge of the shards' partials.
 flp_status validate_forward_partial(int64_t N, int64_t D, int64_t V_local, int64_t vocab_start,
                                     int64_t V_total, flp_dtype x_dtype, const void* hidden,

@@ -101,6 +101,42 @@ def test_hidden_row_offsets_stay_within_32_bits(x, esize):
         "FLP_UNSUPPORTED_SHAPE"
 
 
+def fwd_noalloc(**kw):
+    a = dict(N=N, D=D, V=V, x=BF16, hidden=H, weight=W, bias=B, targets=T, t=I64, temp=TMP,
+             logp=LP, lse=LS, stream=0)
+    a.update(kw)
+    return abi.flp_forward_noalloc(a["N"], a["D"], a["V"], a["x"], a["hidden"], a["weight"],
+                                   a["bias"], a["targets"], a["t"], a["temp"], a["logp"], a["lse"],
+                                   a["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(N=-1), "FLP_INVALID_ARGUMENT"),
+    (dict(x=I64), "FLP_UNSUPPORTED_DTYPE"),
+    (dict(D=48), "FLP_UNSUPPORTED_SHAPE"),
+    (dict(hidden=0), "FLP_INVALID_ARGUMENT"),
+    (dict(logp=0), "FLP_INVALID_ARGUMENT"),
+    (dict(weight=W + 4), "FLP_MISALIGNED"),
+    (dict(logp=H + 64), "FLP_INVALID_ARGUMENT"),          # output inside hidden
+    (dict(lse=LP + 16), "FLP_INVALID_ARGUMENT"),          # two outputs overlap
+    # the workspace of 8440 rows at V = 131072 exceeds the fixed 33 MiB array
+    (dict(N=8440, D=64, V=131072), "FLP_WORKSPACE_TOO_SMALL"),
+    (dict(N=0, hidden=0, targets=0, logp=0), "FLP_OK"),   # empty batch: no-op
+])
+def test_forward_noalloc_gates(kw, expect):
+    assert abi.STATUS_NAMES[fwd_noalloc(**kw)] == expect
+
+
+def test_forward_noalloc_limit():
+    """The fixed array holds the forward workspace of up to 8439 rows at V = 131072 (the
+    rollout batch of 8192 rows fits); one row more does not."""
+    cap = abi.FLP_FORWARD_NOALLOC_MAX_BYTES
+    assert cap == 33 << 20
+    assert abi.flp_forward_workspace_bytes(8439, 2688, 131072) <= cap
+    assert abi.flp_forward_workspace_bytes(8440, 2688, 131072) > cap
+    assert abi.flp_forward_workspace_bytes(8192, 2688, 131072) <= cap
+
+
 def fpart(**kw):
     a = dict(N=N, D=D, VL=512, vs=256, VT=1000, x=BF16, hidden=H, weight=W, bias=B, targets=T,
              t=I64, temp=TMP, part=LP, zt=LS, stream=0)
