@@ -38,6 +38,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <type_traits>
 
 #include <math.h>
 
@@ -274,8 +275,9 @@ __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "m
 // earlier) and every wave must be done reading stage t, whose buffer then receives
 // the loads of stage t + NS.  Small tiles do little work per stage, so they use a
 // deeper ring to keep enough loads in flight.
-template <class E, int BM, int BN, int WM, int WN, int NS = 2>
+template <class E, int BM, int BN, int WM, int WN, int NS = 2, int NSA = NS>
 struct Engine {
+  using TileA = DTile<BM, WM * WN>;
   static constexpr int NW = WM * WN;
   static constexpr int NT = 64 * NW;
   static constexpr int RW = BM / WM;
@@ -283,8 +285,10 @@ struct Engine {
   static constexpr int WMB = RW / 16;
   static constexpr int WNB = CW / 16;
   static constexpr int kSlots = (BM + BN) * 8;  // 16-byte LDS chunks per stage
-  static constexpr size_t kLds = NS * size_t(kSlots) * 16;
+  // NSA buffers of the A operand, NS of B (NSA = NS: one ring of both).
+  static constexpr size_t kLds = (size_t(NSA) * BM + size_t(NS) * BN) * 128;
   static_assert(NS >= 2, "at least two LDS stages");
+  static_assert(NSA == NS || (NS == 2 && NSA == 3), "A ring one deeper than B: 3 and 2 buffers");
   static_assert(RW % 16 == 0 && CW % 16 == 0, "wave tile must be a multiple of 16");
 
   struct Frag {
@@ -298,6 +302,15 @@ struct Engine {
     for (int mb = 0; mb < WMB; ++mb) f.a[mb] = st[fa + mb * 128];
 #pragma unroll
     for (int nb = 0; nb < WNB; ++nb) f.b[nb] = st[BM * 8 + fb + nb * 128];
+  }
+
+  // The same with the A and B fragments in separate buffers.
+  __device__ __forceinline__ static void read2(Frag& f, const u32x4* sa, const u32x4* sb, int fa,
+                                               int fb) {
+#pragma unroll
+    for (int mb = 0; mb < WMB; ++mb) f.a[mb] = sa[fa + mb * 128];
+#pragma unroll
+    for (int nb = 0; nb < WNB; ++nb) f.b[nb] = sb[fb + nb * 128];
   }
 
   __device__ __forceinline__ static void mmas(f32x4_t (&acc)[WMB][WNB], const Frag& f) {
@@ -344,7 +357,7 @@ struct Engine {
     const int wm = wave % WM, wn = wave / WM, i = lane & 15, g = lane >> 4;
     const int nsteps = int(kbytes / kStageBytes);
     const int nst = (nsteps + 1) / 2;
-    DTile<BM, NW> ta;
+    TileA ta;
     DTile<BN, NW> tb;
     ta.init(lda, a_ks, a_rows_valid, lane);
     tb.init(ldb, b_ks, b_rows_valid, lane);
@@ -358,7 +371,11 @@ struct Engine {
       ta.issue(a, t, half, dst, wave);
       tb.issue(b, t, half, dst + BM * 8, wave);
     };
-    if constexpr (NS > 2) {
+    if constexpr (NSA != NS) {
+      static_assert(!ODD, "the split ring serves the GEMMs, whose K is whole 128-byte stages");
+      split(acc, nst, ta, tb, a, b, fa, fb, smem, wave);
+      return;
+    } else if constexpr (NS > 2) {
       deep<ODD>(acc, nst, issue, fa, fb, smem, wave);
       return;
     }
@@ -402,9 +419,9 @@ struct Engine {
   // over the waves in runs of kPer), so each wave waits on its own count: a
   // wave-uniform branch picks the immediate, and every wave then reaches the one
   // barrier.
-  static_assert(NS == 2 || (NS - 1) * (DTile<BM, NW>::kPer + DTile<BN, NW>::kPer) <= 63,
+  static_assert(NS == 2 || (NS - 1) * (TileA::kPer + DTile<BN, NW>::kPer) <= 63,
                 "the loads in flight must fit the vmcnt counter");
-  static constexpr int loads_of(int w) { return DTile<BM, NW>::count(w) + DTile<BN, NW>::count(w); }
+  static constexpr int loads_of(int w) { return TileA::count(w) + DTile<BN, NW>::count(w); }
   // Last wave of the run of waves from w on that issue as many loads as wave w.
   static constexpr int run_end(int w) {
     return w + 1 < NW && loads_of(w + 1) == loads_of(w) ? run_end(w + 1) : w;
@@ -422,6 +439,84 @@ struct Engine {
       wait_own<Stages * loads_of(W)>();
     }
   }
+  // Per-wave wait until at most KA stages of its A loads and KB stages of its B
+  // loads are outstanding.
+  static constexpr int mix_of(int w, int ka, int kb) {
+    return ka * TileA::count(w) + kb * DTile<BN, NW>::count(w);
+  }
+  static constexpr int mix_end(int w, int ka, int kb) {
+    return w + 1 < NW && mix_of(w + 1, ka, kb) == mix_of(w, ka, kb) ? mix_end(w + 1, ka, kb) : w;
+  }
+  template <int KA, int KB, int W = 0>
+  __device__ __forceinline__ static void wait_mix(int wave) {
+    constexpr int Last = mix_end(W, KA, KB);
+    if constexpr (Last + 1 < NW) {
+      if (wave <= Last) {
+        wait_own<mix_of(W, KA, KB)>();
+        return;
+      }
+      wait_mix<KA, KB, Last + 1>(wave);
+    } else {
+      wait_own<mix_of(W, KA, KB)>();
+    }
+  }
+
+  // The split ring: three buffers of the A operand, two of B.  The GEMMs stream
+  // their A operand (dz, dz^T) from HBM once, while B (W^T, hidden^T) is shared by
+  // many workgroups through the caches, so the A loads get two stages of time to
+  // land and the B loads one.  At the barrier of stage t the buffers of stage t
+  // are free and receive B(t + 2), then A(t + 3), in that order: the direct loads
+  // complete in issue order, so waiting until only this wave's A(t + 2) loads may
+  // be outstanding (issued at the previous barrier, after B(t + 1)) guarantees
+  // that all of stage t + 1 has landed.
+  template <class TA, class TB>
+  __device__ __forceinline__ static void split(f32x4_t (&acc)[WMB][WNB], int nst, const TA& ta,
+                                               const TB& tb, const char* a, const char* b, int fa,
+                                               int fb, u32x4* smem, int wave) {
+    u32x4* const sa = smem;
+    u32x4* const sb = smem + NSA * BM * 8;
+    auto issue_a = [&](int t, int buf) { ta.issue(a, t, false, sa + buf * BM * 8, wave); };
+    auto issue_b = [&](int t, int buf) { tb.issue(b, t, false, sb + buf * BN * 8, wave); };
+    issue_a(0, 0);
+    issue_b(0, 0);
+    if (nst > 1) {
+      issue_a(1, 1);
+      issue_b(1, 1);
+    }
+    if (nst > 2) {
+      issue_a(2, 2);
+      wait_mix<2, 1>(wave);  // A(1), B(1), A(2) may be in flight
+    } else if (nst > 1) {
+      wait_mix<1, 1>(wave);
+    } else {
+      wait_own<0>();
+    }
+    barrier_only();
+    Frag f0, f1;
+    read2(f0, sa, sb, fa, fb);
+    int ca = 0, cb = 0;  // buffers of stage t
+    for (int t = 0; t < nst; ++t) {
+      const int na = ca == 2 ? 0 : ca + 1, nb = cb ^ 1;
+      read2(f1, sa + ca * BM * 8, sb + cb * BN * 8, fa ^ 4, fb ^ 4);
+      mmas(acc, f0);
+      interleave();
+      if (t + 1 < nst) {
+        if (t + 2 < nst)
+          wait_mix<1, 0>(wave);  // only A(t + 2) may be in flight
+        else
+          wait_own<0>();
+        barrier_only();
+        if (t + 2 < nst) issue_b(t + 2, cb);
+        if (t + 3 < nst) issue_a(t + 3, ca);
+      }
+      read2(f0, sa + na * BM * 8, sb + nb * BN * 8, fa, fb);
+      mmas(acc, f1);
+      interleave();
+      ca = na;
+      cb = nb;
+    }
+  }
+
   template <bool ODD, class Issue>
   __device__ __forceinline__ static void deep(f32x4_t (&acc)[WMB][WNB], int nst, Issue& issue,
                                               int fa, int fb, u32x4* smem, int wave) {
@@ -813,27 +908,27 @@ __global__ __launch_bounds__(256) void k_logits_bwd(LogitsArgs p) {
 
 // ---- dlogits: recompute the logit tile, dz = G (onehot - p) / T, d_bias partials ------------
 //
-// dz is written token-major (for d_hidden = dz W) and transposed (for d_weight =
-// dz^T hidden), both in the K-blocked layout of the GEMM operands.  A bf16
-// [256 x 256] tile is staged in LDS (256 rows of 512 bytes, each padded by 16
-// bytes), once token-major and once column-major, so that every store covers
-// whole lines.
-struct DzStage {
-  static constexpr int kRowB = kTileCols * 2 + 16;
-  static constexpr size_t kBytes = size_t(kTileCols) * kRowB;
-};
-
-template <class E, int BM, int WM>
-constexpr size_t dz_lds() {
-  using Eng = LogitEngine<E, BM, WM>;
-  return (E::kSize == 2 && DzStage::kBytes > Eng::kLds) ? DzStage::kBytes : Eng::kLds;
-}
+// dz is written token-major (the A operand of d_hidden = dz W) and transposed (the
+// A operand of d_weight = dz^T hidden), both in the K-blocked layout of the GEMM
+// operands.  16-bit inputs write them straight from the registers, every wave
+// store instruction one contiguous 1 KB run (8 rows x one 128-byte K block).
+//
+// K order.  Within every 32-wide block of K, the 16-bit backward GEMMs take their K
+// positions in the order
+//   K position 32 b + 8 g + 4 h + r  <->  index 32 b + 16 h + 4 g + r
+// (g, r = 0..3; h = 0, 1) of the vocabulary (d_hidden) or token (d_weight)
+// dimension: the order in which a lane of the logit tile holds its values, so that
+// each lane's eight values of two adjacent 16-column blocks form one 16-byte chunk
+// of K.  The transposes of W and of hidden (k_transpose16) apply the same order, so
+// every product pairs the same dz, W and hidden entries as in the natural order.
 
 template <class E, int BM, int WM, bool ODD>
 __global__ __launch_bounds__(128 * WM) void k_dz(DzArgs p) {
   using Eng = LogitEngine<E, BM, WM>;
   constexpr int RW = Eng::RW, WMB = Eng::WMB, WNB = Eng::WNB, NT = Eng::NT;
-  constexpr bool kStage = E::kSize == 2 && BM == kTileCols;  // 16-bit: coalesce through LDS
+  constexpr bool kDirect = E::kSize == 2;  // 16-bit: stores straight from the registers
+  static_assert(!kDirect || (BM == kTileCols && WM == 4), "the 16-bit store path is laid out for "
+                                                          "the 256 x 256 tile with 4 x 2 waves");
   extern __shared__ u32x4 smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: tile tests become scalar
@@ -853,13 +948,11 @@ __global__ __launch_bounds__(128 * WM) void k_dz(DzArgs p) {
   Eng::template run<ODD>(acc, reinterpret_cast<const char*>(p.hidden) + row0 * kbytes, kbytes, p.rows - row0,
            reinterpret_cast<const char*>(p.weight) + col0 * kbytes, kbytes, p.V - col0, kbytes,
            smem);
-  __syncthreads();  // every wave is done with the operand stages: LDS is reused below
 
   const int64_t cw = col0 + wn * kHalfCols;
   // Columns of this wave at or past lim are vocabulary padding (lim < 128 only in
   // the last vocabulary tile).
   const int lim = int(p.V - cw < kHalfCols ? p.V - cw : kHalfCols);
-  char* lds = reinterpret_cast<char*>(smem);
   f32x4_t csum[WNB];
   {
     float bcol[WNB][4];
@@ -947,7 +1040,7 @@ __global__ __launch_bounds__(128 * WM) void k_dz(DzArgs p) {
       for (int nb = 0; nb < WNB; ++nb) {
         const f32x4_t d = acc[mb][nb];
         csum[nb] += d;
-        if constexpr (!kStage) {
+        if constexpr (!kDirect) {
           constexpr int KB = 128 / E::kSize;
           const int64_t c = cw + nb * 16 + 4 * g;
           if (p.dz != nullptr) store4<E>(p.dz, kblk<KB>(row, c, p.ldt), d);
@@ -965,58 +1058,94 @@ __global__ __launch_bounds__(128 * WM) void k_dz(DzArgs p) {
       }
     }
   }
-  if constexpr (kStage) {
-    constexpr int kRowB = DzStage::kRowB;
-    constexpr int kChunks = kTileCols * (kTileCols * 2 / 16);  // 16-byte chunks per tile
-    if (p.dz != nullptr) {
-      // Token-major tile: each lane writes its 4 consecutive columns (8 bytes).
+  if constexpr (kDirect) {
+    // Lane (i, g) holds, for row block mb and the column blocks 2 c, 2 c + 1 of its
+    // wave, token i at the vocabulary columns 32 c + 16 h + 4 g + r: in the K order
+    // above, chunk g of the 32-wide step c of that token (16 bytes).
+    //
+    // dz^T: an MFMA multiplies such a chunk by a 0/1 matrix selecting 16 of its 32
+    // columns (column 16 e + n for output column n), which lays the 16 x 16 block out
+    // column-wise: lane (n, g) gets column 16 e + n at tokens 4 g + r.  A 16-bit value
+    // times 1 plus zeros is exact in fp32, so these are the same bits.  The row blocks
+    // 2 q and 2 q + 1 together give the tokens 32 q + 16 h + 4 g + r of one column:
+    // chunk g of its 32-wide token step q.
+    //
+    // Stores.  A 128-byte K block is two such steps.  Lane i < 8 holds chunk g of
+    // step 0 (X) for row i, lane i + 8 the same for row i + 8; their step-1 chunks
+    // (Y) are swapped between the two lanes (lane i ^ 8, a DPP row rotation), after
+    // which one store covers rows 0..7 (lanes i < 8: X at chunk g, lanes i >= 8: the
+    // partner's Y at chunk 4 + g) and another rows 8..15: 8 rows x 128 bytes each.
+    constexpr uint32_t kOne = std::is_same<E, F16>::value ? 0x3C00u : 0x3F80u;  // 1.0
+    // The selection B operand: lane (n, g) supplies rows 8 g .. 8 g + 7 of column n,
+    // and column n selects K slot 8 (n >> 2) + 4 e + (n & 3).
+    u32x4 sel[2];
 #pragma unroll
-      for (int mb = 0; mb < WMB; ++mb)
+    for (int e = 0; e < 2; ++e) {
+      const int jj = g == (i >> 2) ? 4 * e + (i & 3) : -1;
 #pragma unroll
-        for (int nb = 0; nb < WNB; ++nb) {
-          const int tl = wm * RW + mb * 16 + i;
-          const int cl = wn * kHalfCols + nb * 16 + 4 * g;
-          u32x2 w;
-          w.x = pack2<E>(acc[mb][nb][0], acc[mb][nb][1]);
-          w.y = pack2<E>(acc[mb][nb][2], acc[mb][nb][3]);
-          *reinterpret_cast<u32x2*>(lds + tl * kRowB + cl * 2) = w;
-        }
-      __syncthreads();
-      // Streaming stores: dz is read back only by the next GEMM, long after it
-      // has left the caches, so it should not evict the operand tiles.
-      for (int idx = tid; idx < kChunks; idx += NT) {
-        const int tl = idx >> 5, ch = idx & 31;
-        const int64_t row = row0 + tl;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(lds + tl * kRowB + ch * 16);
-        if (row < p.rows)
-          __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.dz) +
-                                                                  kblk<64>(row, col0 + ch * 8, p.ldt)));
-      }
-      __syncthreads();
+      for (int w = 0; w < 4; ++w)
+        sel[e][w] = (jj == 2 * w ? kOne : 0u) | (jj == 2 * w + 1 ? kOne << 16 : 0u);
     }
-    if (p.dzT != nullptr) {
-      // Column-major tile: every lane writes its four values as 2-byte entries of
-      // four column rows (no exchange between lanes).
+    const bool lo = i < 8;
+    // Element offsets, within one 16-row block and one 128-byte K block, of this
+    // lane's 16 bytes in the store of rows 0..7 (o0) and of rows 8..15 (o1).
+    const int o0 = (i & 7) * 64 + (lo ? g : 4 + g) * 8;
+    const int o1 = o0 + 8 * 64 + (lo ? 32 : -32);
+    auto store_pair = [&](uint16_t* base, const u32x4& x, const u32x4& y) {
+      u32x4 z;
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        z[w] = __float_as_uint(lane_xor(__uint_as_float(y[w]), 8));
+      u32x4 s0, s1;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        s0[w] = lo ? x[w] : z[w];
+        s1[w] = lo ? z[w] : x[w];
+      }
+      __builtin_nontemporal_store(s0, reinterpret_cast<u32x4*>(base + o0));
+      __builtin_nontemporal_store(s1, reinterpret_cast<u32x4*>(base + o1));
+    };
+    uint16_t* const dz = reinterpret_cast<uint16_t*>(p.dz);
+    uint16_t* const dzT = reinterpret_cast<uint16_t*>(p.dzT);
+    const int64_t tw = row0 + wm * RW;  // first token of this wave's rows (a multiple of 64)
+#pragma unroll
+    for (int b = 0; b < WNB / 4; ++b) {  // the two 128-byte K blocks of the wave's 128 columns
+      u32x4 f[WMB][2];
 #pragma unroll
       for (int mb = 0; mb < WMB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < WNB; ++nb) {
-          const f32x4_t d = acc[mb][nb];
-          const int tk = wm * RW + mb * 16 + i;
-          const int c = wn * kHalfCols + nb * 16 + 4 * g;
-          const uint32_t p01 = pack2<E>(d[0], d[1]), p23 = pack2<E>(d[2], d[3]);
-          uint16_t* col = reinterpret_cast<uint16_t*>(lds + c * kRowB + tk * 2);
-          col[0] = uint16_t(p01);
-          col[kRowB / 2] = uint16_t(p01 >> 16);
-          col[kRowB] = uint16_t(p23);
-          col[3 * (kRowB / 2)] = uint16_t(p23 >> 16);
+        for (int cc = 0; cc < 2; ++cc) {
+          const int nb = 4 * b + 2 * cc;
+          f[mb][cc].x = pack2<E>(acc[mb][nb][0], acc[mb][nb][1]);
+          f[mb][cc].y = pack2<E>(acc[mb][nb][2], acc[mb][nb][3]);
+          f[mb][cc].z = pack2<E>(acc[mb][nb + 1][0], acc[mb][nb + 1][1]);
+          f[mb][cc].w = pack2<E>(acc[mb][nb + 1][2], acc[mb][nb + 1][3]);
         }
-      __syncthreads();
-      for (int idx = tid; idx < kChunks; idx += NT) {
-        const int cl = idx >> 5, ch = idx & 31;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(lds + cl * kRowB + ch * 16);
-        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.dzT) +
-                                                                kblk<64>(col0 + cl, row0 + ch * 8, p.ldz)));
+      if (dz != nullptr) {
+        const int64_t kb = (cw + 64 * b) / 64;  // K block of columns cw + 64 b .. + 63
+#pragma unroll
+        for (int mb = 0; mb < WMB; ++mb)
+          store_pair(dz + (kb * p.ldt + tw + mb * 16) * 64, f[mb][0], f[mb][1]);
+      }
+      if (dzT != nullptr) {
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            u32x4 t[2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              f32x4_t u0 = {0.f, 0.f, 0.f, 0.f}, u1 = {0.f, 0.f, 0.f, 0.f};
+              mma64<E>(u0, f[2 * q][cc], sel[e]);
+              mma64<E>(u1, f[2 * q + 1][cc], sel[e]);
+              t[q] = u32x4{pack2<E>(u0[0], u0[1]), pack2<E>(u0[2], u0[3]), pack2<E>(u1[0], u1[1]),
+                           pack2<E>(u1[2], u1[3])};
+            }
+            // rows: vocabulary columns cw + 64 b + 32 cc + 16 e + 0..15; K block: the
+            // wave's 64 tokens
+            const int64_t vrow = cw + 64 * b + 32 * cc + 16 * e;
+            store_pair(dzT + ((tw / 64) * p.ldz + vrow) * 64, t[0], t[1]);
+          }
       }
     }
   }
@@ -1068,9 +1197,9 @@ __global__ __launch_bounds__(128 * WM) void k_dz(DzArgs p) {
 //   d_weight: M = V, N = D, K = tokens (padded); A = dz^T, B = hidden^T.
 // LOAD: start from the fp32 accumulator p.acc; STORE: 0 = element type to p.out,
 // 1 = fp32 to p.acc.
-template <class E, int BM, int BN, int WM, int WN, bool LOAD, int STORE, int NS = 2>
+template <class E, int BM, int BN, int WM, int WN, bool LOAD, int STORE, int NS = 2, int NSA = NS>
 __global__ __launch_bounds__(64 * WM * WN) void k_gemm(GemmArgs p) {
-  using Eng = Engine<E, BM, BN, WM, WN, NS>;
+  using Eng = Engine<E, BM, BN, WM, WN, NS, NSA>;
   constexpr int RW = Eng::RW, CW = Eng::CW, WMB = Eng::WMB, WNB = Eng::WNB;
   extern __shared__ u32x4 smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1168,7 +1297,9 @@ __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ src, in
 // The same for 16-bit elements with 16-byte global accesses on both sides: a
 // 64 x 64 tile is read as 8 16-byte chunks per source row and written as 8
 // 16-byte chunks per destination row (one 128-byte K block).  Requires
-// 16-byte aligned source rows and rows_pad a multiple of 64.
+// 16-byte aligned source rows and rows_pad a multiple of 64.  The destination's K
+// positions take the fragment-major order of the 16-bit backward GEMMs: K
+// position 32 b + 8 g + 4 h + r holds source row 32 b + 16 h + 4 g + r.
 __global__ __launch_bounds__(256) void k_transpose16(const uint16_t* __restrict__ src, int64_t rows,
                                                      int64_t rows_pad, int64_t cols, int64_t ld_src,
                                                      uint16_t* __restrict__ dst) {
@@ -1189,9 +1320,13 @@ __global__ __launch_bounds__(256) void k_transpose16(const uint16_t* __restrict_
   for (int p = 0; p < 2; ++p) {
     const int cl = q + 32 * p;
     const int64_t c = c0 + cl, r = r0 + 8 * j;
+    // K positions 8 j + k of the tile: block j >> 2, g = j & 3, h = k >> 2, r = k & 3.
     uint32_t h[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) h[k] = (tile[8 * j + k][cl >> 1] >> (16 * (cl & 1))) & 0xFFFFu;
+    for (int k = 0; k < 8; ++k) {
+      const int src = 32 * (j >> 2) + 16 * (k >> 2) + 4 * (j & 3) + (k & 3);
+      h[k] = (tile[src][cl >> 1] >> (16 * (cl & 1))) & 0xFFFFu;
+    }
     const u32x4 w = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
                      h[6] | (h[7] << 16)};
     if (c < cols && r < rows_pad) *reinterpret_cast<u32x4*>(dst + kblk<64>(c, r, cols)) = w;
@@ -1261,7 +1396,7 @@ hipError_t fwd_dispatch(const FwdArgs& a, hipStream_t s) {
 template <class E, int BM, int WM, bool ODD>
 hipError_t dz_cfg(const DzArgs& a, hipStream_t s) {
   using Eng = LogitEngine<E, BM, WM>;
-  constexpr size_t lds = dz_lds<E, BM, WM>();
+  constexpr size_t lds = Eng::kLds;
   static std::atomic<int> ready[kMaxDevices];
   const hipError_t e = prepare(k_dz<E, BM, WM, ODD>, lds, ready);
   if (e != hipSuccess) return e;
@@ -1270,17 +1405,22 @@ hipError_t dz_cfg(const DzArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <class E, int BM, int BN, int WM, int WN, bool LOAD, int STORE, int NS = 2>
+template <class E, int BM, int BN, int WM, int WN, bool LOAD, int STORE, int NS = 2, int NSA = NS>
 hipError_t gemm_cfg(const GemmArgs& a, hipStream_t s) {
-  using Eng = Engine<E, BM, BN, WM, WN, NS>;
+  using Eng = Engine<E, BM, BN, WM, WN, NS, NSA>;
   static std::atomic<int> ready[kMaxDevices];
-  const hipError_t e = prepare(k_gemm<E, BM, BN, WM, WN, LOAD, STORE, NS>, Eng::kLds, ready);
+  const hipError_t e = prepare(k_gemm<E, BM, BN, WM, WN, LOAD, STORE, NS, NSA>, Eng::kLds, ready);
   if (e != hipSuccess) return e;
   const int64_t blocks = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  hipLaunchKernelGGL((k_gemm<E, BM, BN, WM, WN, LOAD, STORE, NS>), dim3(unsigned(blocks)),
+  hipLaunchKernelGGL((k_gemm<E, BM, BN, WM, WN, LOAD, STORE, NS, NSA>), dim3(unsigned(blocks)),
                      dim3(Eng::NT), Eng::kLds, s, a);
   return hipGetLastError();
 }
+
+// A-operand ring depth of the 256 x 224 backward GEMM tiles (B keeps two buffers):
+// the split ring of Engine::split (d_hidden and d_weight 2 % faster than one ring of
+// two stages, same bits).
+constexpr int kGemmNSA = 3;
 
 // The per-element MFMA chain does not depend on the tile shape, so the GEMM
 // variants may use different tiles and still give the same bits.
@@ -1297,7 +1437,7 @@ hipError_t dx_tiles16(const GemmArgs& a, hipStream_t s) {
   if (a.M <= 128) return gemm_cfg<E, 64, 32, 4, 1, false, 0, 8>(a, s);
   if (a.M <= 512) return gemm_cfg<E, 128, 64, 2, 2, false, 0, 4>(a, s);
   if (a.M <= 1024) return gemm_cfg<E, 128, 128, 2, 2, false, 0, 3>(a, s);
-  return gemm_cfg<E, 256, 224, 4, 2, false, 0>(a, s);
+  return gemm_cfg<E, 256, 224, 4, 2, false, 0, 2, kGemmNSA>(a, s);
 }
 template <class E>
 hipError_t dx_dispatch(const GemmArgs& a, hipStream_t s);
@@ -1319,20 +1459,20 @@ hipError_t dw_dispatch(const GemmArgs& a, hipStream_t s);
 template <>
 hipError_t dw_dispatch<BF16>(const GemmArgs& a, hipStream_t s) {
   if (a.load_acc) {
-    if (a.store_acc) return gemm_cfg<BF16, 256, 224, 4, 2, true, 1>(a, s);
-    return gemm_cfg<BF16, 256, 224, 4, 2, true, 0>(a, s);
+    if (a.store_acc) return gemm_cfg<BF16, 256, 224, 4, 2, true, 1, 2, kGemmNSA>(a, s);
+    return gemm_cfg<BF16, 256, 224, 4, 2, true, 0, 2, kGemmNSA>(a, s);
   }
-  if (a.store_acc) return gemm_cfg<BF16, 256, 224, 4, 2, false, 1>(a, s);
-  return gemm_cfg<BF16, 256, 224, 4, 2, false, 0>(a, s);
+  if (a.store_acc) return gemm_cfg<BF16, 256, 224, 4, 2, false, 1, 2, kGemmNSA>(a, s);
+  return gemm_cfg<BF16, 256, 224, 4, 2, false, 0, 2, kGemmNSA>(a, s);
 }
 template <>
 hipError_t dw_dispatch<F16>(const GemmArgs& a, hipStream_t s) {
   if (a.load_acc) {
-    if (a.store_acc) return gemm_cfg<F16, 256, 224, 4, 2, true, 1>(a, s);
-    return gemm_cfg<F16, 256, 224, 4, 2, true, 0>(a, s);
+    if (a.store_acc) return gemm_cfg<F16, 256, 224, 4, 2, true, 1, 2, kGemmNSA>(a, s);
+    return gemm_cfg<F16, 256, 224, 4, 2, true, 0, 2, kGemmNSA>(a, s);
   }
-  if (a.store_acc) return gemm_cfg<F16, 256, 224, 4, 2, false, 1>(a, s);
-  return gemm_cfg<F16, 256, 224, 4, 2, false, 0>(a, s);
+  if (a.store_acc) return gemm_cfg<F16, 256, 224, 4, 2, false, 1, 2, kGemmNSA>(a, s);
+  return gemm_cfg<F16, 256, 224, 4, 2, false, 0, 2, kGemmNSA>(a, s);
 }
 template <>
 hipError_t dw_dispatch<F32>(const GemmArgs& a, hipStream_t s) {
