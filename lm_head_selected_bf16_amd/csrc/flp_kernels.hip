@@ -710,34 +710,46 @@ __device__ __forceinline__ void fold(float& M, float& S, float m, float s) {
 
 constexpr int kMergeRows = 8, kMergeSegs = 32;
 
+// Latency-bound for small N: every load a thread needs is issued before the first
+// fold (a segment of up to 16 tiles in one batch; the row's target and target
+// logit by the threads that finish the row), so one memory round trip precedes the
+// arithmetic.
+constexpr int kMergeBatch = 16;
+
 __global__ __launch_bounds__(256) void k_merge(MergeArgs p) {
   __shared__ float sm[kMergeSegs][kMergeRows], ss[kMergeSegs][kMergeRows];
   const int rl = threadIdx.x % kMergeRows, seg = threadIdx.x / kMergeRows;
   const int64_t row = int64_t(blockIdx.x) * kMergeRows + rl;
   const int64_t seglen = (p.n_vt + kMergeSegs - 1) / kMergeSegs;
+  const bool fin = seg == 0 && row < p.N;
+  int64_t t = -1;
+  float zt = 0.f;
+  if (fin) {
+    t = load_target(p.targets, p.t64, row);
+    zt = p.zt[row];
+  }
   float M = -INFINITY, S = 0.f;
   if (row < p.N) {
     const int64_t v1 = min(p.n_vt, (seg + 1) * seglen);
-    for (int64_t v0 = seg * seglen; v0 < v1; v0 += 8) {
-      float2 q[8];
+    for (int64_t v0 = seg * seglen; v0 < v1; v0 += kMergeBatch) {
+      float2 q[kMergeBatch];
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+      for (int u = 0; u < kMergeBatch; ++u)
         q[u] = (v0 + u < v1) ? p.part[(v0 + u) * p.N + row] : make_float2(-INFINITY, 0.f);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) fold(M, S, q[u].x, q[u].y);
+      for (int u = 0; u < kMergeBatch; ++u) fold(M, S, q[u].x, q[u].y);
     }
   }
   sm[seg][rl] = M;
   ss[seg][rl] = S;
   __syncthreads();
-  if (seg == 0 && row < p.N) {
+  if (fin) {
     float M2 = -INFINITY, S2 = 0.f;
 #pragma unroll
     for (int k = 0; k < kMergeSegs; ++k) fold(M2, S2, sm[k][rl], ss[k][rl]);
     const float ls = logf(S2);
-    const int64_t t = load_target(p.targets, p.t64, row);
     const bool valid = t >= 0 && t < p.V;
-    p.logp[row] = valid ? (p.zt[row] - M2) - ls : 0.0f;
+    p.logp[row] = valid ? (zt - M2) - ls : 0.0f;
     if (p.lse != nullptr) p.lse[row] = M2 + ls;
   }
 }
