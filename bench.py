@@ -660,6 +660,8 @@ def main() -> int:
         "method_frac_of_peak": round(step_flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "method_frac_of_measured_peak": round(step_flops / (ms / 1e3) / 1e12 / meas, 4),
         "measured_peaks": peaks,
+        "provenance": {"build_info": m.flp_build_info(), "fallback": False,
+                       "library": os.path.relpath(m._abi.LIB_PATH, ROOT)},
         "roofline": roofline,
         "kernels": kernels,
     }

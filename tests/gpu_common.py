@@ -84,3 +84,28 @@ def oracle_backward(inp, grad_out=None, rows=None, need_weight=True, need_bias=T
     return oracle.backward(inp["hidden"], inp["weight"], inp["targets"], go, inp["bias"],
                            inp["temperature"], rows=rows, need_weight=need_weight,
                            need_bias=need_bias)
+
+
+_FLP_X = {torch.bfloat16: 0, torch.float32: 1, torch.float16: 4}
+
+
+def workspace_for_chunk(N, D, V, x_dtype, dw_dtype, rows, need_hidden=True, need_weight=True,
+                        need_bias=True):
+    """The smallest backward workspace with which flp_backward processes `rows` rows per
+    chunk for the requested outputs (found with the library's host-side planner,
+    flp_backward_chunk_rows, which picks the largest chunk that fits)."""
+    from lm_head_selected_bf16_amd import _abi
+    x, dw = _FLP_X[x_dtype], _FLP_X[dw_dtype]
+
+    def chunk(b):
+        return _abi.flp_backward_chunk_rows(N, D, V, x, dw, b, need_hidden, need_weight, need_bias)
+
+    lo, hi = 0, 1 << 40
+    while lo < hi:  # smallest workspace whose chunk is at least `rows`
+        mid = (lo + hi) // 2
+        if chunk(mid) >= rows:
+            hi = mid
+        else:
+            lo = mid + 1
+    assert chunk(lo) == rows, (rows, chunk(lo))
+    return lo

@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import flp_inputs
-from gpu_common import flp, gpu_backward, gpu_forward, inputs, say, to_gpu
+from gpu_common import flp, gpu_backward, gpu_forward, inputs, say, to_gpu, workspace_for_chunk
 
 pytestmark = pytest.mark.gpu
 BF16 = torch.bfloat16
@@ -94,27 +94,33 @@ def test_d_hidden_row_subsets(train_small, n):
 
 
 def test_backward_chunking_is_bit_neutral(train_small):
-    """256-row chunks (fp32 d_weight accumulator across chunks) vs one chunk."""
+    """Several row chunks give exactly the bits of one chunk (PR #555 summary bullets:
+    chunked deterministic backward).  Workspaces are sized with the library's planner so
+    that the chunk counts are what the test says (a bf16 d_weight in several chunks needs
+    the 1.4 GB fp32 accumulator, which at 1100 rows costs more than one whole chunk, so
+    that path is compared at the long-sequence shape)."""
     inp, g, logp, lse = train_small
     m = flp()
     N, D, V = 1100, 2688, 131072
-    one = gpu_backward(g, lse, need_bias=True,
-                       workspace_bytes=m.backward_workspace_bytes(N, D, V, BF16, chunk_rows=N))
-    many = gpu_backward(g, lse, need_bias=True,
-                        workspace_bytes=m.backward_workspace_bytes(N, D, V, BF16, chunk_rows=256))
-    mid = gpu_backward(g, lse, need_bias=True,
-                       workspace_bytes=m.backward_workspace_bytes(N, D, V, BF16, chunk_rows=512))
-    for name, a, b, c in zip(("d_hidden", "d_weight", "d_bias"), one, many, mid):
-        say(f"chunking {name}")
-        assert torch.equal(a, b) and torch.equal(a, c), name
-    # the same with an fp32 d_weight output (accumulates in the caller's buffer)
-    f1 = gpu_backward(g, lse, need_bias=False, dw_dtype=torch.float32,
-                      workspace_bytes=m.backward_workspace_bytes(N, D, V, BF16, torch.float32, N))
-    f2 = gpu_backward(g, lse, need_bias=False, dw_dtype=torch.float32,
-                      workspace_bytes=m.backward_workspace_bytes(N, D, V, BF16, torch.float32, 256))
-    assert torch.equal(f1[1], f2[1])
+    F32 = torch.float32
+    # d_hidden and d_bias: 256-row chunks (5) and 512-row chunks (3) against one chunk
+    one = gpu_backward(g, lse, need_weight=False, need_bias=True)
+    for rows in (256, 512):
+        ws = workspace_for_chunk(N, D, V, BF16, BF16, rows, need_weight=False)
+        dh, _, db = gpu_backward(g, lse, need_weight=False, need_bias=True, workspace_bytes=ws)
+        say(f"chunking {rows} rows: d_hidden, d_bias")
+        assert torch.equal(dh, one[0]) and torch.equal(db, one[2]), rows
+    # fp32 d_weight accumulates in the caller's buffer: 256-row chunks against one chunk
+    f1 = gpu_backward(g, lse, need_bias=True, dw_dtype=F32)
+    ws = workspace_for_chunk(N, D, V, BF16, F32, 256)
+    f2 = gpu_backward(g, lse, need_bias=True, dw_dtype=F32, workspace_bytes=ws)
+    say("chunking 256 rows: fp32 d_weight")
+    for a_, b_ in zip(f1, f2):
+        assert torch.equal(a_, b_)
     # bf16 d_weight is the single rounding of the fp32 one
-    assert torch.equal(f1[1].to(BF16), one[1])
+    full = gpu_backward(g, lse, need_bias=True)
+    assert torch.equal(f1[1].to(BF16), full[1])
+    assert torch.equal(full[0], one[0]) and torch.equal(full[2], one[2])
 
 
 def test_fp16_row_subsets():

@@ -16,6 +16,7 @@ import torch
 
 import flp_inputs
 from gpu_common import (FP32_CELL, LOGP_CELL, REDUCTION_CELL, check_close, flp, gpu_backward,
+                        workspace_for_chunk,
                         gpu_forward, inputs, oracle_backward, oracle_forward, say, to_gpu)
 
 pytestmark = pytest.mark.gpu
@@ -250,4 +251,25 @@ def test_longseq_n65600_multichunk():
     say("case longseq_n65600: N=65600 D=2688 V=131072 bf16, fwd+bwd, 16384-row chunks")
     m = flp()
     ws = m.backward_workspace_bytes(65600, 2688, 131072, BF16, chunk_rows=16384)
+    assert m.flp_backward_chunk_rows(65600, 2688, 131072, m.FLP_BF16, m.FLP_BF16, ws) == 16384
     _train_like("longseq_n65600", 24, ws_bytes=ws)
+
+
+def test_longseq_chunked_equals_one_chunk():
+    """The long sequence's backward in five row chunks (bf16 d_weight through the fp32
+    accumulator across chunks) against one chunk of all 65600 rows (a 33 GiB workspace):
+    every output bit for bit (PR #555 summary bullets: chunking of the deterministic
+    backward is bit-neutral)."""
+    m = flp()
+    inp = inputs("longseq_n65600")
+    g = to_gpu(inp)
+    logp, lse = gpu_forward(g)
+    ws5 = m.backward_workspace_bytes(65600, 2688, 131072, BF16, chunk_rows=16384)
+    ws1 = workspace_for_chunk(65600, 2688, 131072, BF16, BF16, 65792, need_bias=False)
+    say(f"case longseq: 5 chunks ({ws5 / 2**30:.1f} GiB) vs one chunk ({ws1 / 2**30:.1f} GiB)")
+    five = gpu_backward(g, lse, need_bias=False, workspace_bytes=ws5)
+    torch.cuda.synchronize()
+    one = gpu_backward(g, lse, need_bias=False, workspace_bytes=ws1)
+    torch.cuda.synchronize()
+    assert torch.equal(five[0], one[0]), "d_hidden"
+    assert torch.equal(five[1], one[1]), "d_weight"
