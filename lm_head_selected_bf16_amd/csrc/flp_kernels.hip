@@ -598,7 +598,9 @@ __global__ __launch_bounds__(128 * WM) void k_fwd(FwdArgs p) {
   // either buffer (buffer 0 when the stage count is odd): LDS is reused below.
   __syncthreads();
 
-  float* red = reinterpret_cast<float*>(smem);  // [2][BM] row max, then [2][BM] row sums
+  // [2][BM] row max of y = h W^T + b per wave column, [2][BM] row sums, [BM] row max of z
+  static_assert(5 * BM * sizeof(float) <= Eng::kLds, "the row reductions fit the operand ring");
+  float* red = reinterpret_cast<float*>(smem);
   const int64_t cw = col0 + wn * kHalfCols;
   // Columns of this wave at or past lim are vocabulary padding (lim < 128 only in
   // the last vocabulary tile).
@@ -624,15 +626,20 @@ __global__ __launch_bounds__(128 * WM) void k_fwd(FwdArgs p) {
     }
   }
 
+  // The logits are z = y / T with y = h W^T + b; the accumulators become y and 1/T
+  // enters through the exp argument's FMA.
+  // The row max of z is the row max of y times 1/T, bit for bit: rounding is
+  // monotone, so max_j fl(y_j / T) = fl(max_j(y_j) / T).
+  float invT[WMB];
 #pragma unroll
   for (int mb = 0; mb < WMB; ++mb) {
     const int rl = wm * RW + mb * 16 + i;
     const int64_t row = row0 + rl;
-    const float invT = (p.temperature != nullptr && row < p.N) ? 1.0f / p.temperature[row] : 1.0f;
+    invT[mb] = (p.temperature != nullptr && row < p.N) ? 1.0f / p.temperature[row] : 1.0f;
 #pragma unroll
     for (int nb = 0; nb < WNB; ++nb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[mb][nb][r] = (acc[mb][nb][r] + bcol[nb][r]) * invT;
+      for (int r = 0; r < 4; ++r) acc[mb][nb][r] += bcol[nb][r];
     if (lim < kHalfCols) {  // the last vocabulary tile: padding columns drop out
 #pragma unroll
       for (int nb = 0; nb < WNB; ++nb)
@@ -656,13 +663,16 @@ __global__ __launch_bounds__(128 * WM) void k_fwd(FwdArgs p) {
   for (int mb = 0; mb < WMB; ++mb) {
     const int rl = wm * RW + mb * 16 + i;
     const int64_t row = row0 + rl;
-    const float M = fmaxf(red[rl], red[BM + rl]);
+    const float M = fmaxf(red[rl], red[BM + rl]) * invT[mb];  // row max of z
     const float Ml = M * kLog2e;
+    const float k = invT[mb] * kLog2e;
+    if (wn == 0 && g == 0) red[4 * BM + rl] = M;
+    // exp(z - M) = 2^(y (log2 e / T) - M log2 e): one FMA per logit
     float e[WNB][4];
 #pragma unroll
     for (int nb = 0; nb < WNB; ++nb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) e[nb][r] = fast_exp2(fmaf(acc[mb][nb][r], kLog2e, -Ml));
+      for (int r = 0; r < 4; ++r) e[nb][r] = fast_exp2(fmaf(acc[mb][nb][r], k, -Ml));
     float s = lane_sum<WNB>(e);
     f32x2_t q = pair16(s);
     s = q.x + q.y;
@@ -674,12 +684,12 @@ __global__ __launch_bounds__(128 * WM) void k_fwd(FwdArgs p) {
       const int64_t rel = t - cw;
       if (t >= 0 && t < p.V && rel >= 0 && rel < kHalfCols && int((rel & 15) >> 2) == g) {
         const int tnb = int(rel >> 4), tr = int(rel & 3);
-        float zt = 0.f;
+        float yt = 0.f;
 #pragma unroll
         for (int nb = 0; nb < WNB; ++nb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) zt = (nb == tnb && r == tr) ? acc[mb][nb][r] : zt;
-        p.zt[row] = zt;
+          for (int r = 0; r < 4; ++r) yt = (nb == tnb && r == tr) ? acc[mb][nb][r] : yt;
+        p.zt[row] = yt * invT[mb];
       }
     }
   }
@@ -687,7 +697,7 @@ __global__ __launch_bounds__(128 * WM) void k_fwd(FwdArgs p) {
   for (int rl = tid; rl < BM; rl += NT) {
     const int64_t row = row0 + rl;
     if (row < p.N) {
-      const float M = fmaxf(red[rl], red[BM + rl]);
+      const float M = red[4 * BM + rl];
       const float S = red[2 * BM + rl] + red[3 * BM + rl];
       p.part[int64_t(tn) * p.N + row] = make_float2(M, S);
     }
@@ -989,9 +999,15 @@ __global__ __launch_bounds__(128 * WM) void k_dz(DzArgs p) {
             if (nb * 16 + 4 * g + r < lim) bcol[nb][r] = bw[nb * 16 + r];
       }
     }
-    // dz = G (onehot - exp(z - lse)) / T, kept in the accumulator registers.
+    // dz = G (onehot - exp(z - lse)) / T, kept in the accumulator registers, with
+    // z = y / T, y = h W^T + b: the accumulators become y, and
+    // exp(z - lse) = 2^(y (log2 e / T) - lse log2 e) is one FMA and one exp2 per logit.
 #pragma unroll
     for (int mb = 0; mb < WMB; ++mb) {
+#pragma unroll
+      for (int nb = 0; nb < WNB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[mb][nb][r] += bcol[nb][r];
       const int64_t row = row0 + wm * RW + mb * 16 + i;
       const bool rv = row < p.rows;
       const float invT = (p.temperature != nullptr && rv) ? 1.0f / p.temperature[row] : 1.0f;
@@ -999,6 +1015,7 @@ __global__ __launch_bounds__(128 * WM) void k_dz(DzArgs p) {
       const bool valid = t >= 0 && t < p.V;
       const float G = valid ? p.grad_out[row] * invT : 0.f;
       const float L = rv ? p.lse[row] : 0.f;
+      const float k = invT * kLog2e, Ll = L * kLog2e;
       // The target's column within the wave for a valid row, else -1.
       const int64_t trel = t - cw;
       const int tcol = (valid && trel >= 0 && trel < kHalfCols) ? int(trel) : -1;
@@ -1009,26 +1026,19 @@ __global__ __launch_bounds__(128 * WM) void k_dz(DzArgs p) {
       // runs under a branch most waves skip.
       float vt = 0.f;
       if (tcol >= 0) {
-        float at = 0.f, bt = 0.f;
+        float yt = 0.f;
 #pragma unroll
         for (int nb = 0; nb < WNB; ++nb)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            if (nb * 16 + 4 * g + r == tcol) {
-              at = acc[mb][nb][r];
-              bt = bcol[nb][r];
-            }
-        const float z = (at + bt) * invT;
-        vt = G * (1.0f - fast_exp2((z - L) * kLog2e));
+            if (nb * 16 + 4 * g + r == tcol) yt = acc[mb][nb][r];
+        vt = G * (1.0f - fast_exp2(fmaf(yt, k, -Ll)));
       }
       const float nG = -G;
 #pragma unroll
       for (int nb = 0; nb < WNB; ++nb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float z = (acc[mb][nb][r] + bcol[nb][r]) * invT;
-          acc[mb][nb][r] = nG * fast_exp2((z - L) * kLog2e);
-        }
+        for (int r = 0; r < 4; ++r) acc[mb][nb][r] = nG * fast_exp2(fmaf(acc[mb][nb][r], k, -Ll));
       if (tcol >= 0) {
 #pragma unroll
         for (int nb = 0; nb < WNB; ++nb)
@@ -1103,16 +1113,15 @@ __global__ __launch_bounds__(128 * WM) void k_dz(DzArgs p) {
     // lane's 16 bytes in the store of rows 0..7 (o0) and of rows 8..15 (o1).
     const int o0 = (i & 7) * 64 + (lo ? g : 4 + g) * 8;
     const int o1 = o0 + 8 * 64 + (lo ? 32 : -32);
+    // The swap is a DPP row rotation by 8 whose bank mask writes only the lanes that
+    // take the partner's value (banks 2 and 3 = lanes 8..15 for the first store,
+    // banks 0 and 1 for the second); the other lanes keep x.
     auto store_pair = [&](uint16_t* base, const u32x4& x, const u32x4& y) {
-      u32x4 z;
-#pragma unroll
-      for (int w = 0; w < 4; ++w)
-        z[w] = __float_as_uint(lane_xor(__uint_as_float(y[w]), 8));
       u32x4 s0, s1;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        s0[w] = lo ? x[w] : z[w];
-        s1[w] = lo ? z[w] : x[w];
+        s0[w] = uint32_t(__builtin_amdgcn_update_dpp(int(x[w]), int(y[w]), 0x128, 0xF, 0xC, false));
+        s1[w] = uint32_t(__builtin_amdgcn_update_dpp(int(x[w]), int(y[w]), 0x128, 0xF, 0x3, false));
       }
       __builtin_nontemporal_store(s0, reinterpret_cast<u32x4*>(base + o0));
       __builtin_nontemporal_store(s1, reinterpret_cast<u32x4*>(base + o1));
