@@ -178,8 +178,9 @@ __device__ __forceinline__ int64_t load_target(const void* t, int t64, int64_t i
 // receives a contiguous run of logical tiles (sharing its L2), then the run is
 // walked in groups of GM row tiles, row tile fastest, so that the workgroups
 // resident at one time share both operand tiles.  Logits tiles use GM = 8
-// (8 row tiles x 4 vocabulary tiles per XCD at a time); the backward GEMMs use
-// GM = 2 (measured best of 2, 4, 8 and 16 for their 12 column tiles).
+// (8 row tiles x 4 vocabulary tiles per XCD at a time; 4 and 16 measured slower);
+// the backward GEMMs use GM = 1, the 12 column tiles of one row tile in turn
+// (measured best of 1, 2, 4, 8 and 16 with their split LDS ring).
 template <int GM = kGroupM>
 __device__ __forceinline__ void tile_of(int bid, int nbm, int nbn, int& tm, int& tn) {
   const int total = nbm * nbn;
@@ -1227,7 +1228,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(GemmArgs p) {
   const int wm = wave % WM, wn = wave / WM, i = lane & 15, g = lane >> 4;
   const int nbm = int((p.M + BM - 1) / BM), nbn = int((p.N + BN - 1) / BN);
   int tm, tn;
-  tile_of<2>(blockIdx.x, nbm, nbn, tm, tn);
+  tile_of<1>(blockIdx.x, nbm, nbn, tm, tn);
   const int64_t m0 = int64_t(tm) * BM, n0 = int64_t(tn) * BN;
   const int64_t nl = n0 + wn * CW + 4 * g;
 
