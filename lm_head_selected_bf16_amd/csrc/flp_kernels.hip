@@ -276,6 +276,10 @@ __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "m
 // earlier) and every wave must be done reading stage t, whose buffer then receives
 // the loads of stage t + NS.  Small tiles do little work per stage, so they use a
 // deeper ring to keep enough loads in flight.
+// What a peeled pipeline stage does at its barrier (a compile-time tag).
+template <int M>
+using Mode = std::integral_constant<int, M>;
+
 template <class E, int BM, int BN, int WM, int WN, int NS = 2, int NSA = NS>
 struct Engine {
   using TileA = DTile<BM, WM * WN>;
@@ -395,20 +399,24 @@ struct Engine {
     // f0.  After the last stage the other buffer still holds consumed data that
     // no load overwrites any more; reading it (unused) keeps the body free of
     // branches around the fragment reads.
-    auto stage = [&](int t) {
+    //
+    // The stages that issue loads run in a loop of their own whose body has no
+    // branches (one block the scheduler orders as a whole); the last two stages
+    // (barrier only, then neither barrier nor loads) are peeled off.
+    auto stage = [&](int t, auto mode) {
+      constexpr int kMode = decltype(mode)::value;  // 0: barrier + loads, 1: barrier, 2: none
       read(f1, smem + (t & 1) * kSlots, fa ^ 4, fb ^ 4);
       mmas(acc, f0);
       interleave();
-      if (t + 1 < nst) {
-        wait_barrier<0>();
-        if (t + 2 < nst) issue(t + 2);
-      }
+      if constexpr (kMode <= 1) wait_barrier<0>();
+      if constexpr (kMode == 0) issue(t + 2);
       read(f0, smem + ((t + 1) & 1) * kSlots, fa, fb);
       mmas(acc, f1);
       interleave();
     };
-    const int nfull = ODD ? nst - 1 : nst;
-    for (int t = 0; t < nfull; ++t) stage(t);
+    for (int t = 0; t + 2 < nst; ++t) stage(t, Mode<0>{});
+    if (nst >= 2) stage(nst - 2, Mode<1>{});
+    if (!ODD) stage(nst - 1, Mode<2>{});
     if constexpr (ODD) mmas(acc, f0);
   }
 
@@ -496,26 +504,33 @@ struct Engine {
     Frag f0, f1;
     read2(f0, sa, sb, fa, fb);
     int ca = 0, cb = 0;  // buffers of stage t
-    for (int t = 0; t < nst; ++t) {
+    // As in the two-stage ring, the stages that issue both loads run in a loop
+    // without branches, and the last three stages are peeled off.
+    auto stage = [&](int t, auto mode) {
+      // 0: barrier + B(t + 2) + A(t + 3), 1: barrier + B(t + 2), 2: barrier, 3: none
+      constexpr int kMode = decltype(mode)::value;
       const int na = ca == 2 ? 0 : ca + 1, nb = cb ^ 1;
       read2(f1, sa + ca * BM * 8, sb + cb * BN * 8, fa ^ 4, fb ^ 4);
       mmas(acc, f0);
       interleave();
-      if (t + 1 < nst) {
-        if (t + 2 < nst)
-          wait_mix<1, 0>(wave);  // only A(t + 2) may be in flight
-        else
-          wait_own<0>();
-        barrier_only();
-        if (t + 2 < nst) issue_b(t + 2, cb);
-        if (t + 3 < nst) issue_a(t + 3, ca);
-      }
+      if constexpr (kMode <= 1)
+        wait_mix<1, 0>(wave);  // only A(t + 2) may be in flight
+      else if constexpr (kMode == 2)
+        wait_own<0>();
+      if constexpr (kMode <= 2) barrier_only();
+      if constexpr (kMode <= 1) issue_b(t + 2, cb);
+      if constexpr (kMode == 0) issue_a(t + 3, ca);
       read2(f0, sa + na * BM * 8, sb + nb * BN * 8, fa, fb);
       mmas(acc, f1);
       interleave();
       ca = na;
       cb = nb;
-    }
+    };
+    int t = 0;
+    for (; t + 3 < nst; ++t) stage(t, Mode<0>{});
+    if (t + 2 < nst) stage(t++, Mode<1>{});
+    if (t + 1 < nst) stage(t++, Mode<2>{});
+    stage(t, Mode<3>{});
   }
 
   template <bool ODD, class Issue>
@@ -531,26 +546,31 @@ struct Engine {
     Frag f0, f1;
     read(f0, smem, fa, fb);
     int cur = 0;  // buffer of stage t
-    const int nfull = ODD ? nst - 1 : nst;
-    for (int t = 0; t < nfull; ++t) {
+    // 0: wait + barrier + loads of stage t + NS, 1: wait + barrier, 2: wait for all
+    // + barrier, 3: none; the load-issuing stages again form a loop of their own.
+    auto stage = [&](int t, auto mode) {
+      constexpr int kMode = decltype(mode)::value;
       const int nxt = cur + 1 == NS ? 0 : cur + 1;
       read(f1, smem + cur * kSlots, fa ^ 4, fb ^ 4);
       mmas(acc, f0);
       interleave();
-      if (t + 1 < nst) {
-        if (t + NS - 1 < nst) {
-          wait_stages<NS - 2>(wave);
-          barrier_only();
-        } else {
-          wait_barrier<0>();
-        }
-        if (t + NS < nst) issue(t + NS);
+      if constexpr (kMode <= 1) {
+        wait_stages<NS - 2>(wave);
+        barrier_only();
+      } else if constexpr (kMode == 2) {
+        wait_barrier<0>();
       }
+      if constexpr (kMode == 0) issue(t + NS);
       read(f0, smem + nxt * kSlots, fa, fb);
       mmas(acc, f1);
       interleave();
       cur = nxt;
-    }
+    };
+    int t = 0;
+    for (; t + NS < nst; ++t) stage(t, Mode<0>{});
+    if (t + NS - 1 < nst) stage(t++, Mode<1>{});
+    for (; t + 1 < nst; ++t) stage(t, Mode<2>{});
+    if (!ODD) stage(t, Mode<3>{});
     if constexpr (ODD) mmas(acc, f0);
   }
 };
