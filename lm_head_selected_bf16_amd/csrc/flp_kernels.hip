@@ -725,63 +725,88 @@ __global__ __launch_bounds__(128 * WM) void k_fwd(FwdArgs p) {
   }
 }
 
-// ---- merge: ascending fold of the per-tile pairs -> lse, logp --------------------------------
+// ---- merge: per-tile pairs -> lse, logp ------------------------------------------------------
 //
-// 256 threads = 8 rows x 32 segments of vocabulary tiles.  Each thread folds its
-// segment in ascending order, then one thread per row folds the 32 segment
-// results in ascending order.  The topology depends on V only.
-__device__ __forceinline__ void fold(float& M, float& S, float m, float s) {
-  if (m == -INFINITY) return;
-  const float Mn = fmaxf(M, m);
-  const float a = S * fast_exp2((M - Mn) * kLog2e);
-  const float b = s * fast_exp2((m - Mn) * kLog2e);
-  S = a + b;
-  M = Mn;
+// The row max M is the largest tile max (exact in any order).  The sum
+// S = sum_t s_t 2^((m_t - M) log2 e) runs over 256 leaves: leaf j adds the tiles
+// [j L, j L + L) (L = ceil(n_vt / 256)) in ascending order, and the leaves are
+// added by a complete binary tree (pairs, pairs of pairs, ...).  Both depend on the
+// vocabulary only, so a row gets the same bits whatever the batch and whichever
+// of the two workgroup shapes below merges it: R = 1 row per workgroup (one leaf
+// per thread, for small batches) or R = 8 rows (eight leaves per thread).  The tree
+// levels inside a wave are xor butterflies over the lanes of one row (addition is
+// commutative, so both partners hold the same bits), the last two levels combine
+// the four waves.  LL = tiles per leaf when they fit in registers (1 or 2), else 0:
+// the tiles are then read twice (max, then sum).
+constexpr int kMergeLeaves = 256;
+constexpr int64_t kMergeRowMax = 2048;  // batches up to this size: one row per workgroup
+
+__device__ __forceinline__ float merge_term(float2 q, float M) {
+  return q.x == -INFINITY ? 0.f : q.y * fast_exp2((q.x - M) * kLog2e);
 }
 
-constexpr int kMergeRows = 8, kMergeSegs = 32;
-
-// Latency-bound for small N: every load a thread needs is issued before the first
-// fold (a segment of up to 16 tiles in one batch; the row's target and target
-// logit by the threads that finish the row), so one memory round trip precedes the
-// arithmetic.
-constexpr int kMergeBatch = 16;
-
+template <int R, int LL>
 __global__ __launch_bounds__(256) void k_merge(MergeArgs p) {
-  __shared__ float sm[kMergeSegs][kMergeRows], ss[kMergeSegs][kMergeRows];
-  const int rl = threadIdx.x % kMergeRows, seg = threadIdx.x / kMergeRows;
-  const int64_t row = int64_t(blockIdx.x) * kMergeRows + rl;
-  const int64_t seglen = (p.n_vt + kMergeSegs - 1) / kMergeSegs;
-  const bool fin = seg == 0 && row < p.N;
+  constexpr int P = kMergeLeaves / (256 / R);  // leaves per thread
+  __shared__ float sm[4][R], ss[4][R];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rl = tid % R, c = tid / R;  // row in the workgroup, thread of the row
+  const int64_t row = int64_t(blockIdx.x) * R + rl;
+  const bool live = row < p.N;
+  const int64_t L = (p.n_vt + kMergeLeaves - 1) / kMergeLeaves;
+  const int64_t v0 = int64_t(c) * P * L, v1 = min(p.n_vt, v0 + P * L);
+  const bool fin = c == 0 && live;
   int64_t t = -1;
   float zt = 0.f;
   if (fin) {
     t = load_target(p.targets, p.t64, row);
     zt = p.zt[row];
   }
-  float M = -INFINITY, S = 0.f;
-  if (row < p.N) {
-    const int64_t v1 = min(p.n_vt, (seg + 1) * seglen);
-    for (int64_t v0 = seg * seglen; v0 < v1; v0 += kMergeBatch) {
-      float2 q[kMergeBatch];
+  auto tile = [&](int64_t v) {
+    return (live && v < v1) ? p.part[v * p.N + row] : make_float2(-INFINITY, 0.f);
+  };
+  float2 q[LL > 0 ? P * LL : 1];
+  float m = -INFINITY;
+  if constexpr (LL > 0) {
 #pragma unroll
-      for (int u = 0; u < kMergeBatch; ++u)
-        q[u] = (v0 + u < v1) ? p.part[(v0 + u) * p.N + row] : make_float2(-INFINITY, 0.f);
+    for (int u = 0; u < P * LL; ++u) q[u] = tile(v0 + u);
 #pragma unroll
-      for (int u = 0; u < kMergeBatch; ++u) fold(M, S, q[u].x, q[u].y);
+    for (int u = 0; u < P * LL; ++u) m = fmaxf(m, q[u].x);
+  } else {
+    for (int64_t v = v0; v < v1; ++v) m = fmaxf(m, tile(v).x);
+  }
+#pragma unroll
+  for (int k = R; k < 64; k <<= 1) m = fmaxf(m, lane_xor(m, k));
+  if (lane < R) sm[wave][rl] = m;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(sm[0][rl], sm[1][rl]), fmaxf(sm[2][rl], sm[3][rl]));
+  float l[P];
+#pragma unroll
+  for (int k = 0; k < P; ++k) {
+    if constexpr (LL > 0) {
+      l[k] = merge_term(q[k * LL], M);
+#pragma unroll
+      for (int j = 1; j < LL; ++j) l[k] += merge_term(q[k * LL + j], M);
+    } else {
+      l[k] = 0.f;
+      for (int64_t v = v0 + k * L; v < v0 + (k + 1) * L; ++v) l[k] += merge_term(tile(v), M);
     }
   }
-  sm[seg][rl] = M;
-  ss[seg][rl] = S;
+  float sum;
+  if constexpr (P == 8)
+    sum = ((l[0] + l[1]) + (l[2] + l[3])) + ((l[4] + l[5]) + (l[6] + l[7]));
+  else
+    sum = l[0];
+#pragma unroll
+  for (int k = R; k < 64; k <<= 1) sum += lane_xor(sum, k);
+  if (lane < R) ss[wave][rl] = sum;
   __syncthreads();
   if (fin) {
-    float M2 = -INFINITY, S2 = 0.f;
-#pragma unroll
-    for (int k = 0; k < kMergeSegs; ++k) fold(M2, S2, sm[k][rl], ss[k][rl]);
-    const float ls = logf(S2);
+    const float S = (ss[0][rl] + ss[1][rl]) + (ss[2][rl] + ss[3][rl]);
+    const float ls = logf(S);
     const bool valid = t >= 0 && t < p.V;
-    p.logp[row] = valid ? (zt - M2) - ls : 0.0f;
-    if (p.lse != nullptr) p.lse[row] = M2 + ls;
+    p.logp[row] = valid ? (zt - M) - ls : 0.0f;
+    if (p.lse != nullptr) p.lse[row] = M + ls;
   }
 }
 
@@ -1535,10 +1560,25 @@ hipError_t launch_forward(flp_dtype x, const FwdArgs& a, hipStream_t s) {
   return fwd_dispatch<F32>(a, s);
 }
 
+template <int R>
+void merge_rows(const MergeArgs& a, hipStream_t s) {
+  const dim3 grid(unsigned((a.N + R - 1) / R));
+  const int64_t L = (a.n_vt + kMergeLeaves - 1) / kMergeLeaves;
+  if (L == 1)
+    hipLaunchKernelGGL((k_merge<R, 1>), grid, dim3(256), 0, s, a);
+  else if (L == 2)
+    hipLaunchKernelGGL((k_merge<R, 2>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_merge<R, 0>), grid, dim3(256), 0, s, a);
+}
+
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
   ProfScope ps(FLP_K_MERGE, s);
-  hipLaunchKernelGGL(k_merge, dim3(unsigned((a.N + kMergeRows - 1) / kMergeRows)), dim3(256), 0, s,
-                     a);
+  // One row per workgroup while that still gives a few workgroups per compute unit.
+  if (a.N <= kMergeRowMax)
+    merge_rows<1>(a, s);
+  else
+    merge_rows<8>(a, s);
   return hipGetLastError();
 }
 
@@ -1623,7 +1663,7 @@ const char* kernel_ids() {
   return "engine: direct global->LDS (buffer_load_dwordx4 lds, whole lines), 2 LDS stages x 128 B of K "
          "(3-8 for the small dX tiles), "
          "mfma_f32_16x16x32_bf16 | 16x16x32_f16 | 16x16x4f32; k_fwd<BM 32/64/128 x BN 256 2x2 waves, "
-         "BM 256 4x2 waves>; k_merge<8 rows x 32 segments>; k_dz<BM 256 x BN 256, 4x2 waves>; "
+         "BM 256 4x2 waves>; k_merge<1 or 8 rows; 256 leaves, fixed tree>; k_dz<BM 256 x BN 256, 4x2 waves>; "
          "k_gemm dX, dW<256x224, 4x2 waves, K-blocked operands; dX for <= 1024 rows: 64x16, "
          "64x32, 128x64, 128x128>; k_transpose (K-blocked); "
          "k_dbias_fold; k_fill; k_logits_fwd, k_logits_bwd<one wave per row>; "

@@ -102,6 +102,27 @@ def test_small_ragged(k):
     full_check(inp, to_gpu(inp), case[0])
 
 
+def test_vocab_past_512_tiles():
+    """V = 140000: 547 vocabulary tiles, three to each of the merge's 256 leaves (its
+    general path, which reads the tile partials twice), through both merge shapes:
+    2100 rows (eight rows per workgroup) and a 40-row subset (one row per workgroup)
+    match the oracle and give every row the same bits."""
+    case = (BF16, 2100, 64, 140000, 0.1, (0.5, 1.5), torch.int64, 5)
+    say(f"case vocab_past_512_tiles: {case}")
+    inp = small_inputs(case, 90)
+    g = to_gpu(inp)
+    logp, lse = gpu_forward(g)
+    rl, rs = oracle_forward(inp)
+    check_close("logp", logp, rl, **LOGP_CELL)
+    check_close("lse", lse, rs, **LOGP_CELL)
+    idx = flp_inputs.random_rows(2100, 40, seed=5).to(g["hidden"].device)
+    sub = dict(g)
+    for k in ("hidden", "targets", "temperature"):
+        sub[k] = g[k][idx].contiguous()
+    lp, ls = gpu_forward(sub)
+    assert torch.equal(lp, logp[idx]) and torch.equal(ls, lse[idx])
+
+
 @pytest.mark.parametrize("dtype", [BF16, torch.float32])
 def test_targets_at_tile_edges(dtype):
     """Targets placed where the logit-tile epilogues branch: every row's target in
