@@ -579,8 +579,8 @@ struct Engine {
 //
 // Workgroup = WM x 2 waves; wave (wm, wn) owns rows [wm*RW, wm*RW + RW) and the 128
 // vocabulary columns [wn*128, wn*128 + 128) of the BM x 256 tile.
-template <class E, int BM, int WM>
-using LogitEngine = Engine<E, BM, kTileCols, WM, 2>;
+template <class E, int BM, int WM, int NS = 2>
+using LogitEngine = Engine<E, BM, kTileCols, WM, 2, NS>;
 
 // The fixed per-row tree over the 32 values one lane holds of a wave's 128 columns.
 template <int WNB>
@@ -592,9 +592,9 @@ __device__ __forceinline__ float lane_sum(const float (&e)[WNB][4]) {
   return ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
 }
 
-template <class E, int BM, int WM, bool ODD>
+template <class E, int BM, int WM, bool ODD, int NS = 2>
 __global__ __launch_bounds__(128 * WM) void k_fwd(FwdArgs p) {
-  using Eng = LogitEngine<E, BM, WM>;
+  using Eng = LogitEngine<E, BM, WM, NS>;
   constexpr int RW = Eng::RW, WMB = Eng::WMB, WNB = Eng::WNB, NT = Eng::NT;
   extern __shared__ u32x4 smem[];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1429,15 +1429,15 @@ hipError_t prepare(K kernel, size_t lds, std::atomic<int> (&ready)[kMaxDevices])
   return e;
 }
 
-template <class E, int BM, int WM, bool ODD>
+template <class E, int BM, int WM, bool ODD, int NS = 2>
 hipError_t fwd_cfg(const FwdArgs& a, hipStream_t s) {
-  using Eng = LogitEngine<E, BM, WM>;
+  using Eng = LogitEngine<E, BM, WM, NS>;
   static std::atomic<int> ready[kMaxDevices];
-  const hipError_t e = prepare(k_fwd<E, BM, WM, ODD>, Eng::kLds, ready);
+  const hipError_t e = prepare(k_fwd<E, BM, WM, ODD, NS>, Eng::kLds, ready);
   if (e != hipSuccess) return e;
   const int64_t blocks = ((a.N + BM - 1) / BM) * ((a.V + kTileCols - 1) / kTileCols);
-  hipLaunchKernelGGL((k_fwd<E, BM, WM, ODD>), dim3(unsigned(blocks)), dim3(Eng::NT), Eng::kLds, s,
-                     a);
+  hipLaunchKernelGGL((k_fwd<E, BM, WM, ODD, NS>), dim3(unsigned(blocks)), dim3(Eng::NT), Eng::kLds,
+                     s, a);
   return hipGetLastError();
 }
 
@@ -1449,7 +1449,15 @@ bool odd_stages(int64_t D) {
 
 template <class E, bool ODD>
 hipError_t fwd_rows(const FwdArgs& a, hipStream_t s) {
-  if (a.N <= 32) return fwd_cfg<E, 32, 2, ODD>(a, s);
+  if (a.N <= 32) {
+    // Over at most 256 vocabulary tiles (a vocabulary shard) the few workgroups each
+    // wait out a load latency per stage with two stages, so they keep three in flight
+    // (four LDS stages, 147 KB).  Over the full vocabulary the 2-stage tiles, two
+    // workgroups per compute unit, stream W faster.
+    const int64_t vt = (a.V + kTileCols - 1) / kTileCols;
+    if (vt <= 256) return fwd_cfg<E, 32, 2, ODD, 4>(a, s);
+    return fwd_cfg<E, 32, 2, ODD>(a, s);
+  }
   if (a.N <= 64) return fwd_cfg<E, 64, 2, ODD>(a, s);
   if (a.N <= 128) return fwd_cfg<E, 128, 2, ODD>(a, s);
   return fwd_cfg<E, 256, 4, ODD>(a, s);
@@ -1662,7 +1670,7 @@ hipError_t launch_dbias_fold(const float* part, int64_t n_parts, int64_t ldz, in
 const char* kernel_ids() {
   return "engine: direct global->LDS (buffer_load_dwordx4 lds, whole lines), 2 LDS stages x 128 B of K "
          "(3-8 for the small dX tiles), "
-         "mfma_f32_16x16x32_bf16 | 16x16x32_f16 | 16x16x4f32; k_fwd<BM 32/64/128 x BN 256 2x2 waves, "
+         "mfma_f32_16x16x32_bf16 | 16x16x32_f16 | 16x16x4f32; k_fwd<BM 32/64/128 x BN 256 2x2 waves (BM 32: 4 stages over <= 256 vocabulary tiles), "
          "BM 256 4x2 waves>; k_merge<1 or 8 rows; 256 leaves, fixed tree>; k_dz<BM 256 x BN 256, 4x2 waves>; "
          "k_gemm dX, dW<256x224, 4x2 waves, K-blocked operands; dX for <= 1024 rows: 64x16, "
          "64x32, 128x64, 128x128>; k_transpose (K-blocked); "

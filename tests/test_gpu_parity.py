@@ -76,6 +76,11 @@ SMALL = [
     # 128 x 128 tiles over D = 160
     (BF16, 150, 96, 1000, 0.1, (0.5, 1.5), torch.int64, 3),
     (BF16, 600, 160, 777, None, None, torch.int64, 4),
+    # at most 32 rows over at most 256 vocabulary tiles: the forward's four-stage ring,
+    # with an odd number of 64-byte K steps (D = 96: two stages, fewer than the ring;
+    # D = 2080: 33 stages, the last one half)
+    (BF16, 30, 96, 5000, 0.1, (0.5, 1.5), torch.int64, 2),
+    (BF16, 24, 2080, 3000, None, None, torch.int32, 2),
     # the smallest shapes the gates allow: D = 32 (a single half K stage), V = 1
     (BF16, 50, 32, 700, 0.1, None, torch.int64, 2),
     (BF16, 33, 64, 1, 0.1, (0.5, 1.5), torch.int64, 2),
