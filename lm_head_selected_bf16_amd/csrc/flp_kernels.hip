@@ -1022,29 +1022,85 @@ __global__ __launch_bounds__(128 * WM) void k_dz(DzArgs p) {
   // the last vocabulary tile).
   const int lim = int(p.V - cw < kHalfCols ? p.V - cw : kHalfCols);
   f32x4_t csum[WNB];
+  // The per-row inputs of the wave's rows and the bias are all loaded before the
+  // first of them is used (rows past the batch read the last row, whose values are
+  // then not used), so the epilogue waits for one memory round trip, not one per
+  // input and row block.  The branches are wave-uniform and outside the row loops.
+  auto rowc = [&](int mb) {
+    const int64_t row = row0 + wm * RW + mb * 16 + i;
+    return row < p.rows ? row : p.rows - 1;
+  };
+  float rtemp[WMB], rgrad[WMB], rlse[WMB];
+  int64_t rt64[WMB];
+  int32_t rt32[WMB];
+  if (p.t64) {
+#pragma unroll
+    for (int mb = 0; mb < WMB; ++mb) {
+      rt64[mb] = reinterpret_cast<const int64_t*>(p.targets)[rowc(mb)];
+      rt32[mb] = 0;
+    }
+  } else {
+#pragma unroll
+    for (int mb = 0; mb < WMB; ++mb) {
+      rt32[mb] = reinterpret_cast<const int32_t*>(p.targets)[rowc(mb)];
+      rt64[mb] = 0;
+    }
+  }
+#pragma unroll
+  for (int mb = 0; mb < WMB; ++mb) {
+    rgrad[mb] = p.grad_out[rowc(mb)];
+    rlse[mb] = p.lse[rowc(mb)];
+    rtemp[mb] = 1.0f;
+  }
+  if (p.temperature != nullptr) {
+#pragma unroll
+    for (int mb = 0; mb < WMB; ++mb) rtemp[mb] = p.temperature[rowc(mb)];
+  }
+  float bcol[WNB][4];
+#pragma unroll
+  for (int nb = 0; nb < WNB; ++nb) {
+    csum[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) bcol[nb][r] = 0.f;
+  }
+  if (p.bias != nullptr) {
+    const float* bw = p.bias + cw + 4 * g;
+    if (lim == kHalfCols) {  // wave-uniform: every column of the wave exists
+#pragma unroll
+      for (int nb = 0; nb < WNB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) bcol[nb][r] = bw[nb * 16 + r];
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < WNB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (nb * 16 + 4 * g + r < lim) bcol[nb][r] = bw[nb * 16 + r];
+    }
+  }
+  // Nothing computed from the per-row inputs may move above this point (it would
+  // wait for them in front of the bias loads).
+#pragma unroll
+  for (int mb = 0; mb < WMB; ++mb)
+    asm volatile("" : "+v"(rt32[mb]), "+v"(rt64[mb]), "+v"(rtemp[mb]), "+v"(rgrad[mb]), "+v"(rlse[mb]));
+  // Per row block: k = log2(e) / T, L log2(e), G = grad / T (0 for an ignored target)
+  // and the target's column within the wave (-1: not among its columns, -2: ignored).
+  float rk[WMB], rl[WMB], rg[WMB];
+  int rtc[WMB];
+#pragma unroll
+  for (int mb = 0; mb < WMB; ++mb) {
+    const int64_t row = row0 + wm * RW + mb * 16 + i;
+    const bool rv = row < p.rows;
+    const float invT = (p.temperature != nullptr && rv) ? 1.0f / rtemp[mb] : 1.0f;
+    const int64_t t = !rv ? -1 : p.t64 ? rt64[mb] : int64_t(rt32[mb]);
+    const bool valid = t >= 0 && t < p.V;
+    rg[mb] = valid ? rgrad[mb] * invT : 0.f;
+    rl[mb] = (rv ? rlse[mb] : 0.f) * kLog2e;
+    rk[mb] = invT * kLog2e;
+    const int64_t trel = t - cw;
+    rtc[mb] = !valid ? -2 : (trel >= 0 && trel < kHalfCols) ? int(trel) : -1;
+  }
   {
-    float bcol[WNB][4];
-#pragma unroll
-    for (int nb = 0; nb < WNB; ++nb) {
-      csum[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int r = 0; r < 4; ++r) bcol[nb][r] = 0.f;
-    }
-    if (p.bias != nullptr) {
-      const float* bw = p.bias + cw + 4 * g;
-      if (lim == kHalfCols) {  // wave-uniform: every column of the wave exists
-#pragma unroll
-        for (int nb = 0; nb < WNB; ++nb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) bcol[nb][r] = bw[nb * 16 + r];
-      } else {
-#pragma unroll
-        for (int nb = 0; nb < WNB; ++nb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (nb * 16 + 4 * g + r < lim) bcol[nb][r] = bw[nb * 16 + r];
-      }
-    }
     // dz = G (onehot - exp(z - lse)) / T, kept in the accumulator registers, with
     // z = y / T, y = h W^T + b: the accumulators become y, and
     // exp(z - lse) = 2^(y (log2 e / T) - lse log2 e) is one FMA and one exp2 per logit.
@@ -1055,16 +1111,9 @@ __global__ __launch_bounds__(128 * WM) void k_dz(DzArgs p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[mb][nb][r] += bcol[nb][r];
       const int64_t row = row0 + wm * RW + mb * 16 + i;
-      const bool rv = row < p.rows;
-      const float invT = (p.temperature != nullptr && rv) ? 1.0f / p.temperature[row] : 1.0f;
-      const int64_t t = rv ? load_target(p.targets, p.t64, row) : -1;
-      const bool valid = t >= 0 && t < p.V;
-      const float G = valid ? p.grad_out[row] * invT : 0.f;
-      const float L = rv ? p.lse[row] : 0.f;
-      const float k = invT * kLog2e, Ll = L * kLog2e;
-      // The target's column within the wave for a valid row, else -1.
-      const int64_t trel = t - cw;
-      const int tcol = (valid && trel >= 0 && trel < kHalfCols) ? int(trel) : -1;
+      const float G = rg[mb], k = rk[mb], Ll = rl[mb];
+      const bool valid = rtc[mb] != -2;
+      const int tcol = rtc[mb] >= 0 ? rtc[mb] : -1;
       // Every kept logit is G (0 - p) = (-G) p (bit for bit, except that a p that
       // underflows to 0 gives a zero of the other sign); the target's entry,
       // G (1 - p), is taken from the row's logit before the tile is overwritten.
