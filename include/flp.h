@@ -409,7 +409,7 @@ flp_status flp_probe_read(const void* buffer, size_t bytes, void* scratch, size_
  */
 typedef enum flp_kernel_kind {
   FLP_K_FORWARD = 0,    /* logits tile + per-tile (max, sum of exp) + target logit */
-  FLP_K_MERGE = 1,      /* ascending fold of the tile partials -> lse, logp */
+  FLP_K_MERGE = 1,      /* fixed-tree merge of the tile partials -> lse, logp */
   FLP_K_DLOGITS = 2,    /* logits tile recompute -> dz, dz^T, d_bias partials */
   FLP_K_TRANSPOSE = 3,  /* W -> W^T, hidden chunk -> hidden^T (K-blocked) */
   FLP_K_DHIDDEN = 4,    /* d_hidden = dz W */
