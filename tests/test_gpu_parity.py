@@ -107,13 +107,15 @@ def test_small_ragged(k):
     full_check(inp, to_gpu(inp), case[0])
 
 
-def test_vocab_past_512_tiles():
-    """V = 140000: 547 vocabulary tiles, three to each of the merge's 256 leaves (its
-    general path, which reads the tile partials twice), through both merge shapes:
+@pytest.mark.parametrize("V", [60000, 140000])
+def test_merge_shapes_and_leaves(V):
+    """The slab merge's leaf paths through both of its workgroup shapes: V = 60000 has
+    235 vocabulary tiles, one per leaf (tile partials held in registers); V = 140000
+    has 547, three per leaf (the general path, which reads the partials twice).
     2100 rows (eight rows per workgroup) and a 40-row subset (one row per workgroup)
     match the oracle and give every row the same bits."""
-    case = (BF16, 2100, 64, 140000, 0.1, (0.5, 1.5), torch.int64, 5)
-    say(f"case vocab_past_512_tiles: {case}")
+    case = (BF16, 2100, 64, V, 0.1, (0.5, 1.5), torch.int64, 5)
+    say(f"case merge_shapes: {case}")
     inp = small_inputs(case, 90)
     g = to_gpu(inp)
     logp, lse = gpu_forward(g)
